@@ -1,0 +1,136 @@
+/*
+ * sage.h - C ABI of the MI355X (gfx950) quantized attention forward.
+ *
+ * What it computes (the pages: the kernels-community issue "aiter-sage-attention:
+ * SageAttention for AMD RDNA4 (gfx1201)", sections "The kernel" and "What I
+ * have so far", and the "SageAttention-RDNA4 v0.4.0" release notes, "What
+ * changed"):
+ *   - a prologue quantizes Q and K to INT8 per 32-row block and V to FP8 per
+ *     channel; with smooth_k the per-channel key mean, summed in fp64, is
+ *     subtracted from K first;
+ *   - the attention step computes QK^T in INT8 and PV in FP8, both with FP32
+ *     accumulation, and writes BF16;
+ *   - accepted inputs are BF16 [B, S, H, 128] with equal Q/K/V shapes, no
+ *     mask, non-causal; anything else is rejected with an error, never
+ *     silently handled another way.
+ *
+ * Conventions for every call:
+ *   - All calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream of the current device). Device pointers must belong to
+ *     the current device.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronises, and keeps no state between calls.
+ *   - Validation is done on the host before any device call, in this order:
+ *       1. null pointers, negative sizes, non-finite or non-positive sm_scale
+ *          -> SAGE_ERR_INVALID_ARGUMENT;
+ *       2. causal, LSE, dtype other than BF16, D != 128, unequal shapes,
+ *          stride[3] != 1, or a base address / row stride that is not 16-byte
+ *          aligned -> SAGE_ERR_UNSUPPORTED;
+ *       3. workspace smaller than the *_workspace_bytes() figure
+ *          -> SAGE_ERR_WORKSPACE_TOO_SMALL;
+ *       4. current device is not gfx950 (or there is none) -> SAGE_ERR_UNSUPPORTED;
+ *       5. a launch failure -> SAGE_ERR_DEVICE.
+ *     sage_last_error() then returns a thread-local message with details.
+ *   - An empty problem (B*S*H == 0) returns SAGE_OK without launching.
+ *   - Inputs must be finite; non-finite values give unspecified codes.
+ *
+ * Quantized layouts (written by sage_prepare, read by sage_attn). With
+ * S_pad = sage_padded_len(S) (S rounded up to whole key tiles of
+ * sage_kv_tile() = 128 keys) and NB = S_pad / 32:
+ *   q8, k8      int8   [B][H][S_pad][128]  rows >= S are zero
+ *   q_scale,    float  [B][H][NB]          scale of 32-row block n (codes *
+ *   k_scale                                 scale ~ value); blocks >= ceil(S/32) are 0
+ *   v8t         uint8  [B][H][128][S_pad]  OCP FP8 E4M3 codes, channel-major
+ *                                          (keys contiguous); keys >= S are 0
+ *   v_scale     float  [B][H][128]         per-channel scale
+ *   k_mean      float  [B][H][128]         smooth_k: the subtracted mean; else 0
+ * Every array is dense; pointers must be 16-byte aligned.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SAGE_BF16 = 1, SAGE_F16 = 2, SAGE_F32 = 3 } sage_dtype;
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARGUMENT = 1,
+  SAGE_ERR_UNSUPPORTED = 2,
+  SAGE_ERR_WORKSPACE_TOO_SMALL = 3,
+  SAGE_ERR_DEVICE = 4
+} sage_status;
+
+/* A strided 4-D tensor on the device. Logical dimensions are (B, S, H, D);
+ * strides are in elements, so [B,S,H,D] ("NHD") and [B,H,S,D] ("HND")
+ * memory orders are both expressible. stride[3] must be 1. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* sage_dtype */
+  int64_t size[4];
+  int64_t stride[4];
+} sage_tensor;
+
+/* Keys per online-softmax tile (128). The tile schedule is part of the
+ * result: P is requantized against the running maximum after each tile. */
+int sage_kv_tile(void);
+
+/* S rounded up to a multiple of sage_kv_tile(); 0 for S <= 0. */
+int64_t sage_padded_len(int64_t S);
+
+/* Device workspace sage_prepare needs (per-chunk channel statistics). */
+size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k);
+
+/* The prologue (issue, "The kernel"; release notes, "What changed"):
+ *   k_mean[b,h,d] = float( sum_s double(K[b,s,h,d]) / S )   (smooth_k; else 0)
+ *   Q, K' = K - k_mean: per 32-row block a = max|x|, scale = a/127,
+ *     code = rint(x * (127/a)) in [-127, 127] (ties to even; a = 0 gives 0)
+ *   V: per channel a = max_s |V|, scale = a/448, code = E4M3(v * (448/a))
+ *     (round to nearest even; an all-zero channel gives scale 0, codes 0)
+ * q, k, v: BF16 tensors of equal size with D = 128. Outputs in the layouts
+ * above; k_mean may be NULL. ws: device memory of at least
+ * sage_prepare_workspace_bytes() bytes, contents need not be initialised.
+ * The result is deterministic and matches the CPU oracle bit for bit. */
+sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
+                         float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* The attention step (issue, "The kernel") on sage_prepare's outputs:
+ *   t_ij = float(q8_i . k8_j) * ((q_scale[i/32] * k_scale[j/32]) * (sm_scale * log2 e))
+ *   online softmax in FP32 over key tiles of sage_kv_tile() keys in ascending
+ *   order (running max m, alpha = 2^(m - m'), l from unrounded p),
+ *   P requantized to E4M3 as E4M3(448 p) against the running max,
+ *   PV in FP8 with FP32 accumulation,
+ *   O[b,s,h,d] = BF16( o_d * v_scale[d] / (448 l) ).
+ * o: BF16 tensor of logical size (B, S, H, 128), any 16-byte aligned strides
+ * with stride[3] = 1. sm_scale > 0 and finite. */
+sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                      const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                      float sm_scale, const sage_tensor* o, void* stream);
+
+/* Device workspace sage_attn_fused needs: the quantized tensors, their
+ * scales and the prologue's statistics. */
+size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
+
+/* sage_prepare then sage_attn on one stream: the C image of
+ * sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse) (issue,
+ * "What I have so far"). is_causal and return_lse must be 0 and lse NULL
+ * (causal attention and log-sum-exp output are rejected, as on the pages). */
+sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
+                            int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
+                            size_t ws_bytes, void* stream);
+
+const char* sage_status_string(sage_status s);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* sage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

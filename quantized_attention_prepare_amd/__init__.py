@@ -1,0 +1,217 @@
+"""MI355X (gfx950) SageAttention-style quantized attention forward.
+
+A thin ctypes binding over libsage.so (include/sage.h). Every step of the
+computation runs in the library's HIP kernels; this module only turns torch
+tensors into pointers, sizes and strides, allocates outputs and workspace
+with torch, passes torch's current HIP stream, and turns error codes into
+exceptions. There is no fallback: if libsage.so is missing or the device is
+not a gfx950, calls raise.
+
+Entry points (the kernels-community issue "aiter-sage-attention", section
+"What I have so far", names sageattn(q, k, v, tensor_layout, is_causal,
+sm_scale, return_lse) and gfx1201_sage_attention(query, key, value,
+softmax_scale, ...)):
+
+  sageattn(q, k, v, tensor_layout="NHD", is_causal=False, sm_scale=None,
+           return_lse=False, smooth_k=True)
+  gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k=True)
+  prepare(q, k, v, smooth_k)            -> dict of quantized tensors
+  attn(prepared, sm_scale, out=None)    -> BF16 output
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsage.so")
+
+SAGE_BF16 = 1
+SAGE_OK, SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE_TOO_SMALL, SAGE_ERR_DEVICE = range(5)
+HEAD_DIM = 128
+
+
+class SageTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("size", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class SageUnsupported(SageError, NotImplementedError):
+    pass
+
+
+class SageInvalid(SageError, ValueError):
+    pass
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_T = ctypes.POINTER(SageTensor)
+
+
+def lib():
+    """Load libsage.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        # Load torch's HIP runtime first: libsage.so then binds to that same
+        # libamdhip64 (matched by soname) instead of mapping a second runtime
+        # that would compete with torch's for the device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sage_kv_tile.restype = ctypes.c_int
+        L.sage_padded_len.argtypes = [_I]
+        L.sage_padded_len.restype = _I
+        L.sage_prepare_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.c_int]
+        L.sage_prepare_workspace_bytes.restype = ctypes.c_size_t
+        L.sage_fused_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.sage_fused_workspace_bytes.restype = ctypes.c_size_t
+        L.sage_prepare.argtypes = [_T, _T, _T, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.sage_prepare.restype = ctypes.c_int
+        L.sage_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P]
+        L.sage_attn.restype = ctypes.c_int
+        L.sage_attn_fused.argtypes = [_T, _T, _T, _T, ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_int,
+                                      _P, ctypes.c_size_t, _P]
+        L.sage_attn_fused.restype = ctypes.c_int
+        L.sage_status_string.argtypes = [ctypes.c_int]
+        L.sage_status_string.restype = ctypes.c_char_p
+        L.sage_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status == SAGE_OK:
+        return
+    L = lib()
+    msg = f"{L.sage_status_string(status).decode()}: {L.sage_last_error().decode()}"
+    if status == SAGE_ERR_UNSUPPORTED:
+        raise SageUnsupported(status, msg)
+    if status in (SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_WORKSPACE_TOO_SMALL):
+        raise SageInvalid(status, msg)
+    raise SageError(status, msg)
+
+
+def kv_tile() -> int:
+    return int(lib().sage_kv_tile())
+
+
+def padded_len(S: int) -> int:
+    return int(lib().sage_padded_len(S))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.bfloat16: 1, torch.float16: 2, torch.float32: 3}.get(t.dtype, 0)
+
+
+def describe(t, layout: str = "NHD") -> SageTensor:
+    """sage_tensor for a 4-D torch tensor in NHD ([B,S,H,D]) or HND ([B,H,S,D]) order."""
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor")
+    if layout == "NHD":
+        size, stride = list(t.shape), list(t.stride())
+    elif layout == "HND":
+        B, H, S, D = t.shape
+        sb, sh, ss, sd = t.stride()
+        size, stride = [B, S, H, D], [sb, ss, sh, sd]
+    else:
+        raise ValueError(f"tensor_layout must be 'NHD' or 'HND', not {layout!r}")
+    return SageTensor(t.data_ptr(), _dtype_code(t), (ctypes.c_int64 * 4)(*size), (ctypes.c_int64 * 4)(*stride))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None) -> dict:
+    """Run the prologue; returns the quantized tensors in the library's layouts."""
+    import torch
+    tq, tk, tv = describe(q, layout), describe(k, layout), describe(v, layout)
+    B, S, H, D = tq.size
+    Sp = padded_len(S)
+    dev = q.device
+    out = dict(q8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+               k8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+               v8t=torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
+               v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    L = lib()
+    nws = L.sage_prepare_workspace_bytes(B, S, H, D, int(bool(smooth_k)))
+    ws = torch.empty(max(int(nws), 1), dtype=torch.uint8, device=dev)
+    check(L.sage_prepare(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), int(bool(smooth_k)), _ptr(out["q8"]),
+                         _ptr(out["q_scale"]), _ptr(out["k8"]), _ptr(out["k_scale"]), _ptr(out["v8t"]),
+                         _ptr(out["v_scale"]), _ptr(out["k_mean"]), _ptr(ws), nws, _stream(stream)))
+    out["S"] = S
+    out["_ws"] = ws   # keep the workspace alive until the stream is done with it
+    return out
+
+
+def attn(prep: dict, sm_scale: float, out=None, stream=None):
+    """Attention step on prepare()'s output; returns BF16 [B, S, H, 128]."""
+    import torch
+    B, H, Sp, D = prep["q8"].shape
+    S = prep["S"]
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=prep["q8"].device)
+    to = describe(out)
+    check(lib().sage_attn(_ptr(prep["q8"]), _ptr(prep["q_scale"]), _ptr(prep["k8"]), _ptr(prep["k_scale"]),
+                          _ptr(prep["v8t"]), _ptr(prep["v_scale"]), B, S, H, D, float(sm_scale), ctypes.byref(to),
+                          _stream(stream)))
+    return out
+
+
+def fused_workspace_bytes(B: int, S: int, H: int, D: int = HEAD_DIM) -> int:
+    return int(lib().sage_fused_workspace_bytes(B, S, H, D))
+
+
+def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_scale=None, return_lse: bool = False,
+             smooth_k: bool = True, out=None, workspace=None, stream=None):
+    """Quantized attention forward (prologue + attention) on one stream.
+
+    q, k, v: BF16 [B, S, H, 128] ("NHD") or [B, H, S, 128] ("HND"), equal shapes.
+    Causal attention and return_lse are rejected (NotImplementedError).
+    """
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    tq, tk, tv = describe(q, tensor_layout), describe(k, tensor_layout), describe(v, tensor_layout)
+    if out is None:
+        out = torch.empty_like(q)
+    to = describe(out, tensor_layout)
+    B, S, H, D = tq.size
+    L = lib()
+    nws = int(L.sage_fused_workspace_bytes(B, S, H, D))
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+    check(L.sage_attn_fused(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), int(bool(is_causal)),
+                            float(sm_scale), int(bool(return_lse)), None, int(bool(smooth_k)), _ptr(workspace),
+                            workspace.numel(), _stream(stream)))
+    return out
+
+
+def gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k: bool = True):
+    """BF16 [B, S, H, 128] attention with the quantized forward (NHD layout)."""
+    return sageattn(query, key, value, "NHD", False, softmax_scale, False, smooth_k)

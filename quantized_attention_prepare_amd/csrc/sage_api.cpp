@@ -1,0 +1,266 @@
+// C ABI of the quantized attention forward (declared in include/sage.h):
+// argument validation on the host, workspace carving, launches on the
+// caller's stream. Rejections follow the kernels-community issue
+// "aiter-sage-attention", "What I have so far": causal, LSE, non-BF16, head
+// dim other than 128, unequal Q/K/V shapes and the wrong GPU architecture
+// raise an error instead of falling back silently.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/sage.h"
+#include "sage_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sage_status fail(sage_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sage_status fail(sage_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sage_status ok() {
+  g_last_error.clear();
+  return SAGE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Step 1 checks (pointer, sizes) of a BF16 tensor argument.
+sage_status check_tensor_args(const sage_tensor* t, const char* name) {
+  if (!t) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: null tensor descriptor", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->size[i] < 0) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: negative size[%d]", name, i);
+  const int64_t n = t->size[0] * t->size[1] * t->size[2] * t->size[3];
+  if (n > 0 && !t->data) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: null data pointer", name);
+  return SAGE_OK;
+}
+
+// Step 2 checks (what the kernels accept) of a BF16 tensor argument.
+sage_status check_tensor_contract(const sage_tensor* t, const char* name, const int64_t* ref_size) {
+  if (t->dtype != SAGE_BF16) return fail(SAGE_ERR_UNSUPPORTED, "%s: dtype %d is not BF16", name, t->dtype);
+  if (t->size[3] != sage::kHeadDim)
+    return fail(SAGE_ERR_UNSUPPORTED, "%s: head dim %lld is not 128", name, (long long)t->size[3]);
+  if (ref_size)
+    for (int i = 0; i < 4; ++i)
+      if (t->size[i] != ref_size[i])
+        return fail(SAGE_ERR_UNSUPPORTED, "%s: shape differs from q in dim %d (%lld vs %lld)", name, i,
+                    (long long)t->size[i], (long long)ref_size[i]);
+  if (t->stride[3] != 1) return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[3] must be 1", name);
+  for (int i = 0; i < 3; ++i)
+    if (t->stride[i] < 0 || (t->stride[i] % 8) != 0)
+      return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[%d]=%lld is not a non-negative multiple of 8 elements", name, i,
+                  (long long)t->stride[i]);
+  if (!aligned16(t->data)) return fail(SAGE_ERR_UNSUPPORTED, "%s: data pointer not 16-byte aligned", name);
+  return SAGE_OK;
+}
+
+sage_status check_sizes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (B < 0 || S < 0 || H < 0 || D < 0) return fail(SAGE_ERR_INVALID_ARGUMENT, "negative size");
+  return SAGE_OK;
+}
+
+// Step 4: the current device must be a gfx950. Looked up once per device.
+sage_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(SAGE_ERR_UNSUPPORTED, "no HIP device: %s", hipGetErrorString(e));
+  static std::mutex mu;
+  static int known[64] = {0};   // 0 unknown, 1 gfx950, 2 other
+  static char names[64][64];
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 64) return fail(SAGE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  if (!known[dev]) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(SAGE_ERR_UNSUPPORTED, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    snprintf(names[dev], sizeof names[dev], "%s", prop.gcnArchName);
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 && (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':')
+                     ? 1 : 2;
+  }
+  if (known[dev] != 1) return fail(SAGE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, names[dev]);
+  return SAGE_OK;
+}
+
+sage::Bf16View view(const sage_tensor* t) {
+  return sage::Bf16View{static_cast<const uint16_t*>(t->data), t->stride[0], t->stride[1], t->stride[2]};
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the fused call: quantized tensors, scales, then the prologue's own workspace.
+struct FusedWs {
+  int8_t* q8;
+  int8_t* k8;
+  uint8_t* v8t;
+  float* q_scale;
+  float* k_scale;
+  float* v_scale;
+  void* prologue;
+};
+
+size_t fused_bytes(int64_t B, int64_t S, int64_t H, FusedWs* carve, void* base) {
+  const int64_t S_pad = sage::padded_len(S);
+  const size_t bh = (size_t)(B * H);
+  const size_t tens = align256(bh * (size_t)S_pad * sage::kHeadDim);
+  const size_t sc = align256(bh * (size_t)(S_pad / sage::kQBlock) * sizeof(float));
+  const size_t vs = align256(bh * sage::kHeadDim * sizeof(float));
+  sage::PrologueShape ps = sage::prologue_shape(B, S, H);
+  const size_t pro = sage::prologue_ws_bytes(ps);
+  if (carve) {
+    char* p = static_cast<char*>(base);
+    carve->q8 = reinterpret_cast<int8_t*>(p); p += tens;
+    carve->k8 = reinterpret_cast<int8_t*>(p); p += tens;
+    carve->v8t = reinterpret_cast<uint8_t*>(p); p += tens;
+    carve->q_scale = reinterpret_cast<float*>(p); p += sc;
+    carve->k_scale = reinterpret_cast<float*>(p); p += sc;
+    carve->v_scale = reinterpret_cast<float*>(p); p += vs;
+    carve->prologue = p;
+  }
+  return 3 * tens + 2 * sc + vs + pro;
+}
+
+sage_status prepare_impl(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
+                         float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
+  sage::PrologueShape ps = sage::prologue_shape(B, S, H);
+  hipError_t e = sage::launch_prologue(view(q), view(k), view(v), ps, smooth_k ? 1 : 0, q8, q_scale, k8, k_scale, v8t,
+                                       v_scale, k_mean, sage::prologue_ws_carve(ws, ps), stream);
+  (void)ws_bytes;
+  if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_kv_tile(void) { return sage::kKvTile; }
+
+int64_t sage_padded_len(int64_t S) { return sage::padded_len(S); }
+
+size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k) {
+  (void)D;
+  (void)smooth_k;
+  if (B <= 0 || S <= 0 || H <= 0) return 0;
+  return sage::prologue_ws_bytes(sage::prologue_shape(B, S, H));
+}
+
+size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  (void)D;
+  if (B <= 0 || S <= 0 || H <= 0) return 0;
+  return fused_bytes(B, S, H, nullptr, nullptr);
+}
+
+sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
+                         float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
+                         void* ws, size_t ws_bytes, void* stream) {
+  sage_status s;
+  if ((s = check_tensor_args(q, "q")) || (s = check_tensor_args(k, "k")) || (s = check_tensor_args(v, "v"))) return s;
+  const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
+  const bool empty = B * S * H == 0;
+  if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
+    return fail(SAGE_ERR_INVALID_ARGUMENT, "null output pointer");
+  const size_t need = sage_prepare_workspace_bytes(B, S, H, q->size[3], smooth_k);
+  if (!empty && need > 0 && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
+  if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
+      (s = check_tensor_contract(v, "v", q->size)))
+    return s;
+  const void* outs[] = {q8, q_scale, k8, k_scale, v8t, v_scale, k_mean, ws};
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return fail(SAGE_ERR_UNSUPPORTED, "output or workspace pointer not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(SAGE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (empty) return ok();
+  if ((s = check_device())) return s;
+  return prepare_impl(q, k, v, smooth_k, q8, q_scale, k8, k_scale, v8t, v_scale, k_mean, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                      const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                      float sm_scale, const sage_tensor* o, void* stream) {
+  sage_status s;
+  if ((s = check_sizes(B, S, H, D))) return s;
+  if ((s = check_tensor_args(o, "o"))) return s;
+  const bool empty = B * S * H == 0;
+  if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
+    return fail(SAGE_ERR_INVALID_ARGUMENT, "null input pointer");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld is not 128", (long long)D);
+  const int64_t want[4] = {B, S, H, D};
+  if ((s = check_tensor_contract(o, "o", want))) return s;
+  const void* ins[] = {q8, q_scale, k8, k_scale, v8t, v_scale};
+  for (const void* p : ins)
+    if (p && !aligned16(p)) return fail(SAGE_ERR_UNSUPPORTED, "input pointer not 16-byte aligned");
+  if (empty) return ok();
+  if ((s = check_device())) return s;
+  sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
+  hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, sm_scale, ov,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
+                            int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
+                            size_t ws_bytes, void* stream) {
+  sage_status s;
+  if ((s = check_tensor_args(q, "q")) || (s = check_tensor_args(k, "k")) || (s = check_tensor_args(v, "v")) ||
+      (s = check_tensor_args(o, "o")))
+    return s;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
+  const bool empty = B * S * H == 0;
+  const size_t need = sage_fused_workspace_bytes(B, S, H, q->size[3]);
+  if (!empty && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
+  if (is_causal) return fail(SAGE_ERR_UNSUPPORTED, "causal attention is not supported");
+  if (return_lse || lse) return fail(SAGE_ERR_UNSUPPORTED, "log-sum-exp output is not supported");
+  if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
+      (s = check_tensor_contract(v, "v", q->size)) || (s = check_tensor_contract(o, "o", q->size)))
+    return s;
+  if (ws && !aligned16(ws)) return fail(SAGE_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (empty) return ok();
+  if ((s = check_device())) return s;
+  FusedWs w{};
+  fused_bytes(B, S, H, &w, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = prepare_impl(q, k, v, smooth_k, w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, nullptr, w.prologue,
+                        ws_bytes, st)))
+    return s;
+  sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
+  hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, sm_scale, ov, st);
+  if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* sage_status_string(sage_status s) {
+  switch (s) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARGUMENT: return "SAGE_ERR_INVALID_ARGUMENT";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED";
+    case SAGE_ERR_WORKSPACE_TOO_SMALL: return "SAGE_ERR_WORKSPACE_TOO_SMALL";
+    case SAGE_ERR_DEVICE: return "SAGE_ERR_DEVICE";
+  }
+  return "SAGE_ERR_UNKNOWN";
+}
+
+const char* sage_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

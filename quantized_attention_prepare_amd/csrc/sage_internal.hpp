@@ -1,0 +1,62 @@
+// Internal declarations shared by the library's HIP sources (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+constexpr int kHeadDim = 128;   // D
+constexpr int kKvTile = 128;    // keys per online-softmax tile
+constexpr int kQBlock = 32;     // rows per INT8 quantization block
+constexpr int kChunk = 128;     // rows handled by one prologue workgroup pass
+
+inline int64_t padded_len(int64_t S) { return S <= 0 ? 0 : (S + kKvTile - 1) / kKvTile * kKvTile; }
+
+// Strided BF16 input view: element (b, s, h, d) at data[b*sb + s*ss + h*sh + d].
+struct Bf16View {
+  const uint16_t* data;
+  int64_t sb, ss, sh;
+};
+
+struct Bf16OutView {
+  uint16_t* data;
+  int64_t sb, ss, sh;
+};
+
+// Workspace layout of the prologue (per-chunk statistics and per-head results).
+struct PrologueWs {
+  double* ksum_part;   // [B*H][nparts][128]
+  float* vmax_part;    // [B*H][nparts][128]
+  float* kmean;        // [B*H][128]
+  float* vinv;         // [B*H][128]
+};
+
+struct PrologueShape {
+  int64_t B, S, H, S_pad;
+  int chunks_per_wg;   // 128-row chunks folded into one statistics workgroup
+  int64_t nparts;      // statistics partials per head
+};
+
+PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H);
+size_t prologue_ws_bytes(const PrologueShape& ps);
+PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps);
+
+hipError_t launch_prologue(const Bf16View& q, const Bf16View& k, const Bf16View& v, const PrologueShape& ps,
+                           int smooth_k, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t,
+                           float* v_scale, float* k_mean_out, const PrologueWs& ws, hipStream_t stream);
+
+hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                            const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H,
+                            float sm_scale, const Bf16OutView& o, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// float -> BF16 bits, round to nearest even (inputs are finite).
+__device__ inline uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace sage

@@ -18,6 +18,7 @@
  * Tensors are [B,S,H,D] with D fastest; element (b,s,h,d) has linear index
  * ((b*S + s)*H + h)*D + d, and that index is the normal's counter.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -100,24 +101,24 @@ static double* make_table(const synth_spec* sp, int64_t H, int64_t D) {
 static void normal_pair(uint64_t seed, uint64_t p, double* z0, double* z1) {
   const double two_pi = 6.283185307179586476925286766559;
   double u1 = synth_uniform(seed, 2 * p), u2 = synth_uniform(seed, 2 * p + 1);
-  double r = sqrt(-2.0 * log(u1));
-  *z0 = r * cos(two_pi * u2);
-  *z1 = r * sin(two_pi * u2);
+  double r = sqrt(-2.0 * log(u1)), sn, cs;
+  sincos(two_pi * u2, &sn, &cs);
+  *z0 = r * cs;
+  *z1 = r * sn;
 }
 
 /* Fill linear elements [start, end) of a [B,S,H,D] tensor (out points at element 0). */
 void synth_fill(const synth_spec* sp, int64_t S, int64_t H, int64_t D, int64_t start, int64_t end, uint16_t* out) {
   (void)S;
+  if (start >= end) return;
   double* tab = make_table(sp, H, D);
-  int64_t i = start;
-  while (i < end) {
-    double z[2];
-    normal_pair(sp->seed, (uint64_t)(i >> 1), &z[0], &z[1]);
-    for (int64_t j = i; j < end && j < ((i | 1) + 1); ++j) {
-      int64_t d = j % D, h = (j / D) % H;
-      out[j] = to_bf16(transform(sp, tab, j, h, d, D, z[j & 1]));
-    }
-    i = (i | 1) + 1;
+  int64_t d = start % D, h = (start / D) % H; /* coordinates of element i, advanced incrementally */
+  double z[2];
+  normal_pair(sp->seed, (uint64_t)(start >> 1), &z[0], &z[1]);
+  for (int64_t i = start; i < end; ++i) {
+    if (!(i & 1) && i != start) normal_pair(sp->seed, (uint64_t)(i >> 1), &z[0], &z[1]);
+    out[i] = sp->kind == SYNTH_NORMAL ? to_bf16(z[i & 1]) : to_bf16(transform(sp, tab, i, h, d, D, z[i & 1]));
+    if (++d == D) { d = 0; if (++h == H) h = 0; }
   }
   free(tab);
 }

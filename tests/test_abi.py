@@ -1,0 +1,160 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every
+function include/sage.h declares, and validates arguments on the host in the
+documented order before any device call. No compute call is made here; the
+pointers passed are host addresses that the library never dereferences."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_attention_prepare_amd as sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WS_SMALL, DEVICE = range(5)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sage.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = sage.lib()
+    names = declared_functions()
+    assert {"sage_prepare", "sage_attn", "sage_attn_fused", "sage_kv_tile"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_constants_and_sizes():
+    assert sage.kv_tile() == 128
+    assert [sage.padded_len(s) for s in (0, 1, 128, 129, 300)] == [0, 128, 128, 256, 384]
+    L = sage.lib()
+    assert L.sage_fused_workspace_bytes(0, 10, 2, 128) == 0
+    small = L.sage_fused_workspace_bytes(1, 256, 2, 128)
+    big = L.sage_fused_workspace_bytes(1, 32768, 28, 128)
+    assert 0 < small < big
+    # the quantized tensors alone: 3 * B*H*S_pad*128 bytes
+    assert big >= 3 * 28 * 32768 * 128
+    assert L.sage_prepare_workspace_bytes(1, 4096, 28, 128, 1) > 0
+    for s in range(5):
+        assert L.sage_status_string(s).decode().startswith("SAGE_")
+
+
+class Host:
+    """16-byte aligned host buffers that stand in for device pointers."""
+
+    def __init__(self):
+        self.keep = []
+
+    def buf(self, nbytes=4096, misalign=0):
+        a = np.zeros(nbytes + 64, np.uint8)
+        self.keep.append(a)
+        base = (a.ctypes.data + 15) & ~15
+        return ctypes.c_void_p(base + misalign)
+
+    def tensor(self, size=(1, 64, 2, 128), dtype=1, stride=None, misalign=0):
+        if stride is None:
+            B, S, H, D = size
+            stride = (S * H * D, H * D, D, 1)
+        return sage.SageTensor(self.buf(misalign=misalign).value, dtype, (ctypes.c_int64 * 4)(*size),
+                               (ctypes.c_int64 * 4)(*stride))
+
+
+def fused(h, q=None, k=None, v=None, o=None, causal=0, sm=0.088, lse_flag=0, lse=None, ws=None, ws_bytes=None):
+    q = q or h.tensor()
+    k = k or h.tensor()
+    v = v or h.tensor()
+    o = o or h.tensor()
+    B, S, H, D = q.size
+    need = sage.lib().sage_fused_workspace_bytes(B, S, H, D)
+    ws = h.buf() if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return sage.lib().sage_attn_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o), causal, sm,
+                                      lse_flag, lse, 1, ws, ws_bytes, None)
+
+
+def last_error():
+    return sage.lib().sage_last_error().decode()
+
+
+def test_fused_validation_order_on_host():
+    h = Host()
+    # 1. invalid arguments
+    assert sage.lib().sage_attn_fused(None, None, None, None, 0, 0.1, 0, None, 1, None, 0, None) == INVALID
+    assert fused(h, sm=float("nan")) == INVALID
+    assert fused(h, sm=0.0) == INVALID
+    assert fused(h, sm=-1.0) == INVALID
+    bad = h.tensor()
+    bad.size[1] = -1
+    assert fused(h, q=bad) == INVALID
+    assert fused(h, ws=ctypes.c_void_p(0)) == INVALID
+    # invalid beats unsupported
+    assert fused(h, causal=1, sm=float("inf")) == INVALID
+    # 2. unsupported contract
+    assert fused(h, causal=1) == UNSUPPORTED and "causal" in last_error()
+    assert fused(h, lse_flag=1) == UNSUPPORTED
+    assert fused(h, lse=ctypes.c_void_p(h.buf().value)) == UNSUPPORTED
+    assert fused(h, q=h.tensor(dtype=2), k=h.tensor(dtype=2), v=h.tensor(dtype=2), o=h.tensor(dtype=2)) == UNSUPPORTED
+    d64 = (1, 64, 2, 64)
+    assert fused(h, q=h.tensor(d64), k=h.tensor(d64), v=h.tensor(d64), o=h.tensor(d64)) == UNSUPPORTED
+    assert fused(h, k=h.tensor((1, 65, 2, 128))) == UNSUPPORTED and "shape" in last_error()
+    assert fused(h, v=h.tensor(stride=(64 * 256, 256, 128, 2))) == UNSUPPORTED
+    assert fused(h, o=h.tensor(stride=(64 * 256, 260, 128, 1))) == UNSUPPORTED
+    assert fused(h, q=h.tensor(misalign=2)) == UNSUPPORTED and "aligned" in last_error()
+    # 3. workspace
+    assert fused(h, ws_bytes=10) == WS_SMALL
+    # unsupported beats a small workspace
+    assert fused(h, causal=1, ws_bytes=10) == UNSUPPORTED
+    # 4. with everything valid, the device check is last: no GPU here
+    rc = fused(h)
+    assert rc == UNSUPPORTED and ("device" in last_error().lower())
+
+
+def test_empty_problem_returns_ok_without_device():
+    h = Host()
+    z = (2, 0, 3, 128)
+    assert fused(h, q=h.tensor(z), k=h.tensor(z), v=h.tensor(z), o=h.tensor(z), ws=ctypes.c_void_p(0), ws_bytes=0) == OK
+
+
+def test_prepare_and_attn_validation_on_host():
+    h = Host()
+    L = sage.lib()
+    q, k, v = h.tensor(), h.tensor(), h.tensor()
+    outs = [h.buf() for _ in range(7)]
+    need = L.sage_prepare_workspace_bytes(1, 64, 2, 128, 1)
+
+    def prep(q=q, k=k, v=v, outs=outs, ws=None, ws_bytes=need):
+        return L.sage_prepare(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1, *outs, ws or h.buf(), ws_bytes, None)
+
+    assert prep(outs=[ctypes.c_void_p(0)] + outs[1:]) == INVALID
+    assert prep(k=h.tensor(dtype=3)) == UNSUPPORTED
+    assert prep(ws_bytes=need - 1) == WS_SMALL
+    assert prep() == UNSUPPORTED and "device" in last_error().lower()
+
+    o = h.tensor()
+    ptrs = [h.buf() for _ in range(6)]
+
+    def at(B=1, S=64, H=2, D=128, sm=0.1, o=o, ptrs=ptrs):
+        return L.sage_attn(*ptrs, B, S, H, D, sm, ctypes.byref(o), None)
+
+    assert at(S=-1) == INVALID
+    assert at(ptrs=[ctypes.c_void_p(0)] + ptrs[1:]) == INVALID
+    assert at(sm=float("nan")) == INVALID
+    assert at(D=64) == UNSUPPORTED
+    assert at(S=65) == UNSUPPORTED          # o's shape differs from (B, S, H, D)
+    assert at() == UNSUPPORTED and "device" in last_error().lower()
+
+
+def test_python_binding_raises_typed_errors():
+    with pytest.raises(sage.SageUnsupported):
+        sage.check(UNSUPPORTED)
+    with pytest.raises(ValueError):
+        sage.check(INVALID)
+    with pytest.raises(ValueError):
+        sage.check(WS_SMALL)
+    with pytest.raises(RuntimeError):
+        sage.check(DEVICE)
