@@ -24,8 +24,8 @@
  *       1. null pointers, negative sizes, non-finite or non-positive sm_scale
  *          -> SAGE_ERR_INVALID_ARGUMENT;
  *       2. causal, LSE, dtype other than BF16, D != 128, unequal shapes,
- *          stride[3] != 1, or a base address / row stride that is not 16-byte
- *          aligned -> SAGE_ERR_UNSUPPORTED;
+ *          stride[3] != 1, a base address / row stride that is not 16-byte
+ *          aligned, or S > 2^25 (33,554,432 tokens) -> SAGE_ERR_UNSUPPORTED;
  *       3. workspace smaller than the *_workspace_bytes() figure
  *          -> SAGE_ERR_WORKSPACE_TOO_SMALL;
  *       4. current device is not gfx950 (or there is none) -> SAGE_ERR_UNSUPPORTED;

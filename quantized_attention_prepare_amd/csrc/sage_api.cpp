@@ -59,6 +59,8 @@ sage_status check_tensor_contract(const sage_tensor* t, const char* name, const 
         return fail(SAGE_ERR_UNSUPPORTED, "%s: shape differs from q in dim %d (%lld vs %lld)", name, i,
                     (long long)t->size[i], (long long)ref_size[i]);
   if (t->stride[3] != 1) return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[3] must be 1", name);
+  if (t->size[1] > sage::kMaxSeq)
+    return fail(SAGE_ERR_UNSUPPORTED, "%s: sequence length %lld exceeds 2^25", name, (long long)t->size[1]);
   for (int i = 0; i < 3; ++i)
     if (t->stride[i] < 0 || (t->stride[i] % 8) != 0)
       return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[%d]=%lld is not a non-negative multiple of 8 elements", name, i,

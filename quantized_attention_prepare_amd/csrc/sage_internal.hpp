@@ -9,6 +9,7 @@ constexpr int kHeadDim = 128;   // D
 constexpr int kKvTile = 128;    // keys per online-softmax tile
 constexpr int kQBlock = 32;     // rows per INT8 quantization block
 constexpr int kChunk = 128;     // rows handled by one prologue workgroup pass
+constexpr int64_t kMaxSeq = int64_t(1) << 25;   // a head's quantized K or V (128 * S_pad bytes) stays below 4 GiB
 
 inline int64_t padded_len(int64_t S) { return S <= 0 ? 0 : (S + kKvTile - 1) / kKvTile * kKvTile; }
 
