@@ -126,24 +126,21 @@ def cpu_baseline(w, budget_s: float = 12.0):
     prep = oracle.prepare_head(qh, kh, vh, w.smooth_k)
     t_prep = time.perf_counter() - t0
     rows_done = 0
-    chunk = nthreads
     t_attn = 0.0
-    rng_rows = synth.sample_rows(w, 100000)
-    rows_all = [int(s) for b, h, s in rng_rows if b == 0 and h == 0] or list(range(w.S))
+    start = int(synth.sample_rows(w, 1)[0, 2])
     with ThreadPoolExecutor(nthreads) as ex:
-        while t_attn < budget_s and rows_done < len(rows_all):
-            batch = rows_all[rows_done:rows_done + chunk]
+        while t_attn < budget_s and rows_done < w.S:
+            batch = [(start + rows_done + i) % w.S for i in range(nthreads)]
             t1 = time.perf_counter()
             list(ex.map(lambda r: oracle.attn_rows_head(prep, [r], w.sm_scale), batch))
             t_attn += time.perf_counter() - t1
             rows_done += len(batch)
-            chunk = min(4 * chunk, max(nthreads, int(rows_done * (budget_s - t_attn) / max(t_attn, 1e-9))))
-            chunk = max(nthreads, chunk - chunk % nthreads)
     ops = 4.0 * rows_done * w.S * w.D
     t_share = t_prep * rows_done / w.S
     return {"value": ops / (t_attn + t_share) / 1e12, "unit": "TFLOPS", "cores": nthreads, "kind": "oracle",
             "sample": f"{w.name}: oracle prologue of head (0,0) ({w.S} rows, {t_prep:.2f} s, charged pro rata) + "
-                      f"quantized attention of {rows_done} seeded query rows of that head ({t_attn:.2f} s); "
+                      f"quantized attention of {rows_done} consecutive query rows of that head from a seeded start "
+                      f"({t_attn:.2f} s); "
                       f"{nthreads} threads"}
 
 
@@ -155,6 +152,8 @@ def main():
     ap.add_argument("--workload", default="C3")
     ap.add_argument("--others", default="C1,C2,C4,C5", help="comma list of further workloads to report ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 512 MiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -163,6 +162,15 @@ def main():
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 5}))
+        return
 
     w = synth.WORKLOADS[args.workload]
     r = measure(w, args.steps, args.warmup)
