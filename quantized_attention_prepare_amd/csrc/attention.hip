@@ -75,8 +75,17 @@ constexpr int kBufferWord3 = 0x00020000;          // raw (untyped) buffer access
 // every copy); tile and row offsets go in the 32-bit scalar offset and the
 // lane offset in one vector register.
 // K tile t: 128 keys x 128 B, contiguous in k8 (head extent S_pad * 128 B).
+// The LDS destination goes through an empty asm so that its per-instruction
+// addresses are formed next to each copy instead of being precomputed for
+// every buffer and kept live in scalar registers across the loop.
+SAGE_INLINE uint8_t* opaque_lds(uint8_t* dst) {
+  uint32_t a = (uint32_t)(uintptr_t)LDS_PTR(dst);
+  asm volatile("" : "+s"(a));
+  return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t)a;
+}
 SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t, const uint32_t (&lane_off)[kCopyInstr],
                         int wave) {
+  dst = opaque_lds(dst);
 #pragma unroll
   for (int i = 0; i < kCopyInstr; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(dst + 1024 * (kCopyInstr * wave + i)), 16, lane_off[i],
@@ -86,6 +95,7 @@ SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t, const ui
 // (head extent 128 * S_pad B).
 SAGE_INLINE void load_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rv, int t, uint32_t S_pad,
                         const uint32_t (&lane_off)[kCopyInstr], int wave) {
+  dst = opaque_lds(dst);
 #pragma unroll
   for (int i = 0; i < kCopyInstr; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(dst + 1024 * (kCopyInstr * wave + i)), 16, lane_off[i],
@@ -107,28 +117,10 @@ SAGE_INLINE float max_xor32(float v) {
 // Per-wave online-softmax state and output accumulators.
 struct WaveState {
   v16f oacc[4];   // O^T blocks: channels 32*d + 8(v/4) + 4h + v%4 of this lane's query
-  v16i sacc[4];   // scores of the tile whose softmax is next (4 blocks of 32 keys)
   v8i pk[2];      // FP8 probabilities of the tile whose PV is next (two 64-key halves)
   float m_run;    // running max (log2 units)
   float l_run;    // this lane-half's share of 448 * sum p
 };
-
-// PV of one tile: O^T[ch][q] += V^T[ch][key] P^T[key][q] over two 64-key
-// halves; the four output channel blocks are independent MFMAs.
-SAGE_INLINE void pv_tile(WaveState& st, const uint8_t* vbuf, int half, int col) {
-  const int fv = (col >> 1) & 7;   // f(ch) for ch = 32 d + col: 32 d does not change bits 1-3
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint8_t* vrow = vbuf + (32 * d + col) * kKvTile;
-      union { v8i v; v4i q[2]; } a;
-      a.q[0] = *reinterpret_cast<const v4i*>(vrow + (((4 * kc + half) ^ fv) * 16));
-      a.q[1] = *reinterpret_cast<const v4i*>(vrow + (((4 * kc + 2 + half) ^ fv) * 16));
-      st.oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, st.pk[kc], st.oacc[d], 0, 0, 0, 0, 0, 0);
-    }
-  }
-}
 
 // INT8 scores S^T = K . Q^T of one tile into sacc: row pi(col) of each 32-key
 // block, channels 32s + 16h .. +15; the four score blocks are independent
@@ -155,79 +147,191 @@ SAGE_INLINE void qk_tile(v16i (&sacc)[4], const uint8_t* kbuf, const uint8_t* qr
 
 // Softmax step for one tile: issues the next tile's score MFMAs, then the
 // online update of the running max and sum, FP8 probabilities into pk,
-// rescale of O; on return sacc holds the next tile's scores.
+// rescale of O; the next tile's scores go to snext.
 // cblk[kb] = (q_scale * k_scale) * sm_scale * log2 e of the tile's 32-key
 // blocks. nvalid < 128 marks a ragged last tile: the padded keys' scores are
 // replaced with INT32_MIN (never above a valid score since |acc| <= 2^21),
 // blocks made only of padding come with cblk = +inf (probability exactly 0),
 // and in the partly padded block the padded keys' probability, which only
 // matters for l (their V codes are 0), is subtracted from l afterwards.
-SAGE_INLINE void softmax_step(WaveState& st, const float (&cblk)[4], int nvalid, int half, const uint8_t* kbuf_next,
-                              const uint8_t* qrow, int col, int prow) {
-  // the next tile's score MFMAs go out first and execute under this softmax
-  v16i snext[4];
-  qk_tile(snext, kbuf_next, qrow, half, col, prow);
-  __builtin_amdgcn_sched_barrier(0);
-  const int kbase = 16 * half;   // key offset of this lane's first key in each 32-key block
+SAGE_INLINE int max3i(int a, int b, int c) { return max(max(a, b), c); }
+
+#define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// V^T operand of PV MFMA (kc, d): channel 32d + col, keys 64kc + 32(j/16) + 16h + j%16.
+SAGE_INLINE v8i v_operand(const uint8_t* vbuf, int kc, int d, int half, int col, int fv) {
+  const uint8_t* vrow = vbuf + (32 * d + col) * kKvTile;
+  union { v8i v; v4i q[2]; } a;
+  a.q[0] = *reinterpret_cast<const v4i*>(vrow + (((4 * kc + half) ^ fv) * 16));
+  a.q[1] = *reinterpret_cast<const v4i*>(vrow + (((4 * kc + 2 + half) ^ fv) * 16));
+  return a.v;
+}
+
+// Max of t = float(acc) * c over the lane's 16 keys of one 32-key block: a
+// tree of three-input maxima on the integer accumulators; float(max acc) * c
+// is the max of the products because c >= 0 and rounding is monotone.
+SAGE_INLINE float block_max(const v16i& x, float c) {
+  const int a0 = max3i(x[0], x[1], x[2]), a1 = max3i(x[3], x[4], x[5]), a2 = max3i(x[6], x[7], x[8]);
+  const int a3 = max3i(x[9], x[10], x[11]), a4 = max3i(x[12], x[13], x[14]);
+  const int im = max(max3i(a0, a1, a2), max3i(a3, a4, x[15]));
+  return (float)im * c;
+}
+
+// Probabilities of 4 consecutive keys (group g of block kb): 448 p = exp2(t - moff)
+// with t = float(acc) * c, summed into ps, packed to FP8 into pk.
+SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v8i (&pk)[2], float (&ps)[4]) {
+  float p[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[4 * g + u], c, -moff));
+    ps[u] += p[u];
+  }
+  const int j = 16 * (kb & 1) + 4 * g;   // k-slot of p[0] within the 64-key half-tile
+  int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+  dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
+  pk[kb >> 1][j >> 2] = dw;
+}
+
+// One iteration, as a fixed sequence of slots separated by scheduling fences,
+// each slot holding at most one MFMA and a run of VALU work that issues while
+// the MFMA executes:
+//   slots 1-8   PV of the previous tile (its probabilities in pk, its V tile in
+//               vbuf_prev), with the maximum of this tile's scores and then the
+//               exp2 of blocks 0 and 1 (whose FP8 codes go to pk[0] once the
+//               MFMAs that read the previous pk[0] have been issued);
+//   slots 9-24  the INT8 score MFMAs of the next tile, with the exp2 of blocks
+//               2 and 3, l, and the rescale of O (the previous PV is complete by
+//               then).
+// The LDS operands of each MFMA are read one slot ahead. kHasPrev is false for
+// the first tile. cblk[kb] = (q_scale * k_scale) * sm_scale * log2 e of the
+// tile's 32-key blocks. nvalid < 128 marks a ragged last tile: padded keys'
+// scores become INT32_MIN (below every valid score since |acc| <= 2^21), blocks
+// made only of padding come with cblk = +inf (probability exactly 0), and in
+// the partly padded block the padded keys' probability, which only matters for
+// l (their V codes are 0), is subtracted from l afterwards.
+template <bool kHasPrev>
+SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], const float (&cblk)[4], int nvalid,
+                                const uint8_t* vbuf_prev, const uint8_t* kbuf_next, const uint8_t* qrow, int half,
+                                int col, int prow) {
+  const int kbase = 16 * half;
+  const int fk = ((prow >> 1) & 3) | (((prow >> 4) & 1) << 2);   // K swizzle of rows 32 kb + prow
+  const int fq = (col >> 1) & 7;                                 // Q swizzle of row col
+  const int fv = (col >> 1) & 7;                                 // V swizzle of rows 32 d + col
+  const uint8_t* krow = kbuf_next + prow * kHeadDim;
+  // ---- slot 0: first V operand; tail masking; max of blocks 0, 1
+  v8i vop;
+  if (kHasPrev) vop = v_operand(vbuf_prev, 0, 0, half, col, fv);
   if (nvalid < kKvTile) {
+    // Only the last tile gets here. The empty asm hides that nvalid is then
+    // the loop-invariant length of the last tile, which would otherwise move
+    // the 64 key-index comparisons out of the loop into live lane masks; the
+    // selection uses sign masks rather than comparisons for the same reason.
+    int nv = nvalid - kbase;
+    asm volatile("" : "+v"(nv));
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (32 * kb + kbase + v >= nvalid) st.sacc[kb][v] = INT32_MIN;
-  }
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    int m8[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) m8[v] = max(st.sacc[kb][v], st.sacc[kb][v + 8]);
-    const int im = max(max(max(m8[0], m8[1]), max(m8[2], m8[3])), max(max(m8[4], m8[5]), max(m8[6], m8[7])));
-    // the block max of t = float(acc) * c is float(max acc) * c because c >= 0
-    // and rounding is monotone
-    tmax = fmaxf(tmax, (float)im * cblk[kb]);
-  }
-  tmax = max_xor32(tmax);
-  const float m_new = fmaxf(st.m_run, tmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
-  const float moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
-
-  // 16 independent partial sums keep the additions off one serial chain
-  float ps[4][4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int v = 0; v < 16; v += 4) {
-      float p[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)st.sacc[kb][v + u], cblk[kb], -moff));
-        ps[kb][u] = v == 0 ? p[u] : ps[kb][u] + p[u];
+      for (int v = 0; v < 16; ++v) {
+        const int keep = (32 * kb + v - nv) >> 31;   // all ones for a valid key
+        sc[kb][v] = (sc[kb][v] & keep) | (INT32_MIN & ~keep);
       }
-      const int j = 16 * (kb & 1) + v;   // k-slot of p[0] within the 64-key half-tile
-      int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
-      st.pk[kb >> 1][j >> 2] = dw;
+  }
+  float tmax = fmaxf(block_max(sc[0], cblk[0]), block_max(sc[1], cblk[1]));
+  SAGE_FENCE();
+#define SAGE_PV_SLOT(KC_, D_, NKC_, ND_, WORK_)                                                            \
+  {                                                                                                         \
+    if (kHasPrev) {                                                                                         \
+      st.oacc[D_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, st.pk[KC_], st.oacc[D_], 0, 0, 0, \
+                                                                    0, 0, 0);                               \
+      if ((NKC_) >= 0) vop = v_operand(vbuf_prev, NKC_, ND_, half, col, fv);                                \
+    }                                                                                                       \
+    WORK_;                                                                                                  \
+    SAGE_FENCE();                                                                                           \
+  }
+  float m_new, alpha, moff;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#define SAGE_EXP(KB_, G_) exp_group(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
+  SAGE_PV_SLOT(0, 0, 0, 1, tmax = fmaxf(tmax, fmaxf(block_max(sc[2], cblk[2]), block_max(sc[3], cblk[3]))))
+  SAGE_PV_SLOT(0, 1, 0, 2, {
+    tmax = max_xor32(tmax);
+    m_new = fmaxf(st.m_run, tmax);
+    alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
+    moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
+  })
+  SAGE_PV_SLOT(0, 2, 0, 3, (void)0)
+  SAGE_PV_SLOT(0, 3, 1, 0, (void)0)
+  // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
+  SAGE_PV_SLOT(1, 0, 1, 1, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
+  SAGE_PV_SLOT(1, 1, 1, 2, { SAGE_EXP(0, 2); SAGE_EXP(0, 3); })
+  SAGE_PV_SLOT(1, 2, 1, 3, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
+  v4i qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
+  v4i kop;
+  SAGE_PV_SLOT(1, 3, -1, 0, {
+    kop = *reinterpret_cast<const v4i*>(krow + (((0 + half) ^ fk) * 16));
+    SAGE_EXP(1, 2);
+    SAGE_EXP(1, 3);
+  })
+#undef SAGE_PV_SLOT
+  // ---- slots 9-24: score MFMAs of the next tile (s outer, kb inner)
+#define SAGE_QK_SLOT(S_, KB_, NS_, NKB_, WORK_)                                                         \
+  {                                                                                                      \
+    const v16i z = {};                                                                                   \
+    snext[KB_] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop, (S_) == 0 ? z : snext[KB_], 0, 0, 0);   \
+    if ((NS_) >= 0) {                                                                                    \
+      if ((NS_) != (S_)) qop = *reinterpret_cast<const v4i*>(qrow + (((2 * (NS_) + half) ^ fq) * 16));   \
+      kop = *reinterpret_cast<const v4i*>(krow + 32 * (NKB_) * kHeadDim + (((2 * (NS_) + half) ^ fk) * 16)); \
+    }                                                                                                    \
+    WORK_;                                                                                               \
+    SAGE_FENCE();                                                                                        \
+  }
+  SAGE_QK_SLOT(0, 0, 0, 1, SAGE_EXP(2, 0))
+  SAGE_QK_SLOT(0, 1, 0, 2, (void)0)
+  SAGE_QK_SLOT(0, 2, 0, 3, SAGE_EXP(2, 1))
+  SAGE_QK_SLOT(0, 3, 1, 0, (void)0)
+  SAGE_QK_SLOT(1, 0, 1, 1, SAGE_EXP(2, 2))
+  SAGE_QK_SLOT(1, 1, 1, 2, (void)0)
+  SAGE_QK_SLOT(1, 2, 1, 3, SAGE_EXP(2, 3))
+  SAGE_QK_SLOT(1, 3, 2, 0, (void)0)
+  SAGE_QK_SLOT(2, 0, 2, 1, SAGE_EXP(3, 0))
+  SAGE_QK_SLOT(2, 1, 2, 2, (void)0)
+  SAGE_QK_SLOT(2, 2, 2, 3, SAGE_EXP(3, 1))
+  SAGE_QK_SLOT(2, 3, 3, 0, (void)0)
+  SAGE_QK_SLOT(3, 0, 3, 1, SAGE_EXP(3, 2))
+  SAGE_QK_SLOT(3, 1, 3, 2, (void)0)
+  SAGE_QK_SLOT(3, 2, 3, 3, SAGE_EXP(3, 3))
+  SAGE_QK_SLOT(3, 3, -1, 0, {
+    float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (nvalid < kKvTile && (nvalid & 31)) {
+      const int kbp = nvalid >> 5;   // the partly padded block
+      const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - nvalid));
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, cblk[kbp], -moff));
+      if (nmask > 0) psum -= (float)nmask * pm;
     }
+    st.l_run = alpha * st.l_run + psum;
+    st.m_run = m_new;
+  })
+#undef SAGE_QK_SLOT
+#undef SAGE_EXP
+  // Rescale O to the new maximum (the previous tile's PV has completed by
+  // now), only when some lane's maximum moved: alpha exactly 1 multiplies by
+  // one, and after the first tiles that is the usual case.
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st.oacc[d][v] *= alpha;
   }
-  float psum = ((ps[0][0] + ps[0][1]) + (ps[0][2] + ps[0][3])) + ((ps[1][0] + ps[1][1]) + (ps[1][2] + ps[1][3])) +
-               (((ps[2][0] + ps[2][1]) + (ps[2][2] + ps[2][3])) + ((ps[3][0] + ps[3][1]) + (ps[3][2] + ps[3][3])));
-  if (nvalid < kKvTile && (nvalid & 31)) {
-    const int kbp = nvalid >> 5;   // the partly padded block
-    const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - nvalid));
-    const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, cblk[kbp], -moff));
-    if (nmask > 0) psum -= (float)nmask * pm;
-  }
-  st.l_run = alpha * st.l_run + psum;
-  // Unconditional: skipping it when every alpha is 1 would need a branch
-  // around the accumulators, which costs more registers than the multiplies.
+}
+
+// PV of the last tile, after the loop.
+SAGE_INLINE void pv_tile(WaveState& st, const uint8_t* vbuf, int half, int col) {
+  const int fv = (col >> 1) & 7;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) st.oacc[d][v] *= alpha;
-  st.m_run = m_new;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) st.sacc[kb] = snext[kb];
+    for (int d = 0; d < 4; ++d)
+      st.oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_operand(vbuf, kc, d, half, col, fv), st.pk[kc],
+                                                                   st.oacc[d], 0, 0, 0, 0, 0, 0);
 }
 
 __global__ void __launch_bounds__(kThreads, 2)
@@ -305,33 +409,46 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const int ntiles = (int)(S_pad / kKvTile);
   const int last_valid = (int)(S - (int64_t)(ntiles - 1) * kKvTile);   // valid keys in the last tile (1..128)
 
-  // K(0), K(1), V(0) in; scores of tile 0.
+  // K(0), K(1) in; scores of tile 0.
   load_k(KBUF(0), rk, 0, k_lane_off, wave);
   if (ntiles > 1) load_k(KBUF(1), rk, 1, k_lane_off, wave);
-  load_v(VBUF(0), rv, 0, spad32, v_lane_off, wave);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  qk_tile(st.sacc, KBUF(0), qrow, half, col, prow);
+  v16i sa[4], sb[4];   // scores of the current and the next tile; they swap roles every iteration
+  qk_tile(sa, KBUF(0), qrow, half, col, prow);
   float4 ksv = *reinterpret_cast<const float4*>(ks);   // k_scale of the four blocks of the current tile
 
-  // Iteration t: softmax of tile t (with the scores of tile t+1 computed under
-  // it), PV of tile t. On entry K(t+1) and V(t) must be in LDS; K(t+2) and
-  // V(t+1) are copied into the buffers K(t) and V(t-1) occupied. After the last
-  // tile the score MFMAs read stale K bytes whose scores are never used.
-  for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
-    __syncthreads();                 // ... everyone's; K(t) and V(t-1) are no longer read
-    if (t + 2 < ntiles) load_k(KBUF(t & 1), rk, t + 2, k_lane_off, wave);
-    if (t + 1 < ntiles) load_v(VBUF((t + 1) & 1), rv, t + 1, spad32, v_lane_off, wave);
-    const int nvalid = t == ntiles - 1 ? last_valid : kKvTile;
-    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};
-    float cblk[4];   // (q_scale * k_scale) * sm_scale * log2 e; +inf for a block made only of padding
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nvalid ? INFINITY : (qs * kss[kb]) * sl2;
-    if (t + 1 < ntiles) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t + 1));
-    softmax_step(st, cblk, nvalid, half, KBUF((t + 1) & 1), qrow, col, prow);
-    pv_tile(st, VBUF(t & 1), half, col);
+  // Iteration t: PV of tile t-1, softmax of tile t, scores of tile t+1. On
+  // entry K(t+1) and V(t-1) must be in LDS; K(t+2) goes to the buffer K(t)
+  // occupied and V(t) to the one V(t-2) occupied. After the last tile the
+  // score MFMAs read stale K bytes whose scores are never used.
+#define SAGE_ITERATION(T_, HAS_PREV_, CUR_, NEXT_)                                                             \
+  {                                                                                                            \
+    const int t_ = (T_);                                                                                       \
+    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                      \
+    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                  \
+    if (t_ + 2 < ntiles) load_k(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                   \
+    load_v(VBUF(t_ & 1), rv, t_, spad32, v_lane_off, wave);                                                    \
+    const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                                \
+    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                         \
+    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block made only of padding */        \
+    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nvalid ? INFINITY : (qs * kss[kb]) * sl2;             \
+    if (t_ + 1 < ntiles) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                            \
+    tile_iteration<HAS_PREV_>(st, CUR_, NEXT_, cblk, nvalid, VBUF((t_ + 1) & 1), KBUF((t_ + 1) & 1), qrow,     \
+                              half, col, prow);                                                                \
   }
+  SAGE_ITERATION(0, false, sa, sb)
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    SAGE_ITERATION(t, true, sb, sa)
+    SAGE_ITERATION(t + 1, true, sa, sb)
+  }
+  if (t < ntiles) SAGE_ITERATION(t, true, sb, sa)
+#undef SAGE_ITERATION
+  // PV of the last tile
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  pv_tile(st, VBUF((ntiles - 1) & 1), half, col);
 
   // ---- epilogue: O = o * v_scale / (448 l)
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
