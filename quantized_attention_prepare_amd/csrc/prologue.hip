@@ -12,8 +12,8 @@
 //            global statistic), quantizes K too when smooth_k is off, and
 //            writes per-chunk partial channel statistics (fp64 key sums,
 //            fp32 V absolute maxima);
-//   finalize one small workgroup per head folds the partials in a fixed order
-//            into k_mean, v_scale and 448/amax;
+//   finalize one workgroup per head folds the partials in a fixed order into
+//            k_mean, v_scale and 448/amax;
 //   quant    second pass over K (smooth_k) and V in reverse chunk order, so
 //            the most recently read data is re-read from the memory-side cache
 //            first; V codes are transposed through LDS into channel-major rows.
@@ -158,17 +158,35 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
 }
 
-__global__ void __launch_bounds__(kHeadDim)
+// One workgroup per head: eight slices of threads each fold every eighth
+// partial (loads kept in flight by unrolling), then the eight slice results
+// are folded in slice order. The order is fixed, so the result is the same on
+// every run.
+constexpr int kFinalizeSlices = 8;
+
+__global__ void __launch_bounds__(kHeadDim * kFinalizeSlices)
 finalize_kernel(int64_t S, int64_t nparts, int smooth_k, const double* __restrict__ ksum_part,
                 const float* __restrict__ vmax_part, float* __restrict__ kmean, float* __restrict__ vinv,
                 float* __restrict__ v_scale, float* __restrict__ k_mean_out) {
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % kHeadDim, j = threadIdx.x / kHeadDim;
   double s = 0.0;
   float a = 0.0f;
-  for (int64_t p = 0; p < nparts; ++p) {
+#pragma unroll 8
+  for (int64_t p = j; p < nparts; p += kFinalizeSlices) {
     s += ksum_part[(bh * nparts + p) * kHeadDim + d];
     a = fmaxf(a, vmax_part[(bh * nparts + p) * kHeadDim + d]);
+  }
+  __shared__ double s_sum[kFinalizeSlices][kHeadDim];
+  __shared__ float s_max[kFinalizeSlices][kHeadDim];
+  s_sum[j][d] = s;
+  s_max[j][d] = a;
+  __syncthreads();
+  if (j != 0) return;
+#pragma unroll
+  for (int i = 1; i < kFinalizeSlices; ++i) {
+    s += s_sum[i][d];
+    a = fmaxf(a, s_max[i][d]);
   }
   float km = smooth_k ? (float)(s / (double)S) : 0.0f;
   kmean[bh * kHeadDim + d] = km;
@@ -304,8 +322,8 @@ hipError_t launch_prologue(const Bf16View& q, const Bf16View& k, const Bf16View&
                      ws.vmax_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(kHeadDim), 0, stream, ps.S, ps.nparts, smooth_k,
-                     ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, v_scale, k_mean_out);
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(kHeadDim * kFinalizeSlices), 0, stream, ps.S,
+                     ps.nparts, smooth_k, ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, v_scale, k_mean_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(quant_kernel, dim3((unsigned)(BH * nchunks)), dim3(kThreads), 0, stream, k, v, ps.H, ps.S,
