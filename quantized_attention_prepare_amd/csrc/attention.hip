@@ -187,7 +187,10 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
     ps[u] += p[u];
   }
   const int j = 16 * (kb & 1) + 4 * g;   // k-slot of p[0] within the 64-key half-tile
-  int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+  // the first conversion writes bytes 0-1 and the second bytes 2-3, so the word
+  // they start from does not matter: p[0]'s own register serves (0 would cost
+  // a move per word)
+  int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
   dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
   pk[kb >> 1][j >> 2] = dw;
 }
