@@ -113,14 +113,27 @@ sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, 
                       const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                       float sm_scale, const sage_tensor* o, void* stream);
 
+/* sage_attn that also writes each row's log-sum-exp, an extension beyond the
+ * pages (whose sageattn rejects return_lse): the natural log of the softmax
+ * normaliser of the dequantized scores s_ij = t_ij ln 2, taken from the final
+ * running maximum m and l as  lse[b][h][s] = m ln 2 + ln l  (fp32, [B][H][S]
+ * contiguous, 4-byte aligned, caller-owned; NULL -> SAGE_ERR_INVALID_ARGUMENT).
+ * With smooth_k the scores are those against the mean-subtracted keys, as the
+ * softmax's are: they differ from the unsmoothed scores by sm_scale * q_i . k_mean
+ * per row, which a caller merging partial results across key shards must add. */
+sage_status sage_attn_lse(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                          const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                          float sm_scale, const sage_tensor* o, float* lse, void* stream);
+
 /* Device workspace sage_attn_fused needs: the quantized tensors, their
  * scales and the prologue's statistics. */
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /* sage_prepare then sage_attn on one stream: the C image of
  * sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse) (issue,
- * "What I have so far"). is_causal and return_lse must be 0 and lse NULL
- * (causal attention and log-sum-exp output are rejected, as on the pages). */
+ * "What I have so far"). is_causal must be 0 (causal attention is rejected, as
+ * on the pages). return_lse = 1 also writes lse as sage_attn_lse does (lse
+ * non-NULL); return_lse = 0 requires lse NULL (else SAGE_ERR_INVALID_ARGUMENT). */
 sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
                             int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
                             size_t ws_bytes, void* stream);

@@ -63,9 +63,9 @@ def lib():
         L.oracle_quant_block_int8.restype = ctypes.c_float
         L.oracle_prepare_head.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P, _P, _P]
         L.oracle_prepare_head.restype = ctypes.c_int
-        L.oracle_attn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, ctypes.c_float, _I, _P, _I, _P, _P]
+        L.oracle_attn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, ctypes.c_float, _I, _P, _I, _P, _P, _P]
         L.oracle_attn_rows.restype = ctypes.c_int
-        L.oracle_exact_rows.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_double, _P, _I, _P]
+        L.oracle_exact_rows.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_double, _P, _I, _P, _P]
         L.oracle_exact_rows.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -171,11 +171,13 @@ def prepare(q: np.ndarray, k: np.ndarray, v: np.ndarray, smooth_k: bool, heads=N
 
 
 # ------------------------------------------------------------ attention
-def attn_rows_head(prep_head: dict, rows, sm_scale: float, T: int = KV_TILE, want_f32: bool = False):
+def attn_rows_head(prep_head: dict, rows, sm_scale: float, T: int = KV_TILE, want_f32: bool = False,
+                   want_lse: bool = False):
     """Quantized attention for the given query rows of one head.
 
     prep_head holds that head's q8 [S,D], q_scale, k8, k_scale, v8t [D,S_pad],
-    v_scale.  Returns BF16 bits [n, D] (and the pre-rounding float values).
+    v_scale.  Returns BF16 bits [n, D], then (if asked) the pre-rounding float
+    values and the rows' log-sum-exp of the dequantized scores (float [n]).
     """
     q8 = np.ascontiguousarray(prep_head["q8"])
     S, D = q8.shape
@@ -188,38 +190,48 @@ def attn_rows_head(prep_head: dict, rows, sm_scale: float, T: int = KV_TILE, wan
     qs = np.ascontiguousarray(prep_head["q_scale"], dtype=np.float32)
     vs = np.ascontiguousarray(prep_head["v_scale"], dtype=np.float32)
     k8 = np.ascontiguousarray(prep_head["k8"])
+    lse = np.empty(n, np.float32) if want_lse else None
     rc = lib().oracle_attn_rows(_ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v8t), v8t.shape[1], _ptr(vs), S, D,
-                                float(sm_scale), int(T), _ptr(rows), n, _ptr(of), _ptr(ob))
+                                float(sm_scale), int(T), _ptr(rows), n, _ptr(of), _ptr(ob), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments")
-    return (ob, of) if want_f32 else ob
+    extra = ([of] if want_f32 else []) + ([lse] if want_lse else [])
+    return tuple([ob] + extra) if extra else ob
 
 
 def head_of(prep: dict, b: int, h: int) -> dict:
     return {k: prep[k][b, h] for k in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale", "k_mean")}
 
 
-def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None, chunk: int = 64):
+def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None, chunk: int = 64,
+         want_lse: bool = False):
     """Quantized attention over full-tensor prologue outputs.
 
-    rows=None computes every row and returns BF16 bits [B, S, H, D].
-    rows = int array [n, 3] of (b, h, s) returns BF16 bits [n, D].
+    rows=None computes every row and returns BF16 bits [B, S, H, D] (and, with
+    want_lse, the log-sum-exp float [B, H, S]).
+    rows = int array [n, 3] of (b, h, s) returns BF16 bits [n, D] (and float [n]).
     """
     B, H, S, D = prep["q8"].shape
     if rows is None:
         out = np.empty((B, S, H, D), np.uint16)
+        lse_all = np.empty((B, H, S), np.float32) if want_lse else None
         jobs = [(b, h, s0) for b in range(B) for h in range(H) for s0 in range(0, S, chunk)]
 
         def job(j):
             b, h, s0 = j
             r = np.arange(s0, min(S, s0 + chunk), dtype=np.int64)
-            out[b, s0:s0 + r.size, h, :] = attn_rows_head(head_of(prep, b, h), r, sm_scale, T)
+            res = attn_rows_head(head_of(prep, b, h), r, sm_scale, T, want_lse=want_lse)
+            if want_lse:
+                out[b, s0:s0 + r.size, h, :], lse_all[b, h, s0:s0 + r.size] = res
+            else:
+                out[b, s0:s0 + r.size, h, :] = res
 
         with ThreadPoolExecutor(nthreads or threads()) as ex:
             list(ex.map(job, jobs))
-        return out
+        return (out, lse_all) if want_lse else out
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], D), np.uint16)
+    lse_rows = np.empty(rows.shape[0], np.float32) if want_lse else None
     groups = {}
     for idx, (b, h, s) in enumerate(rows):
         groups.setdefault((int(b), int(h)), []).append(idx)
@@ -230,24 +242,30 @@ def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None
 
     def job2(j):
         b, h, idxs = j
-        out[idxs] = attn_rows_head(head_of(prep, b, h), rows[idxs, 2], sm_scale, T)
+        res = attn_rows_head(head_of(prep, b, h), rows[idxs, 2], sm_scale, T, want_lse=want_lse)
+        if want_lse:
+            out[idxs], lse_rows[idxs] = res
+        else:
+            out[idxs] = res
 
     with ThreadPoolExecutor(nthreads or threads()) as ex:
         list(ex.map(job2, jobs))
-    return out
+    return (out, lse_rows) if want_lse else out
 
 
-def exact_rows_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, sm_scale: float) -> np.ndarray:
-    """fp64 exact attention rows of one head from dense [S, D] BF16 arrays."""
+def exact_rows_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, sm_scale: float, want_lse: bool = False):
+    """fp64 exact attention rows of one head from dense [S, D] BF16 arrays
+    (and, if asked, each row's ln sum_j exp(q.k_j * sm_scale))."""
     q, k, v = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v))
     S, D = q.shape
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     out = np.empty((rows.size, D), np.float64)
+    lse = np.empty(rows.size, np.float64) if want_lse else None
     rc = lib().oracle_exact_rows(_ptr(q), _ptr(k), _ptr(v), S, D, D, float(sm_scale), _ptr(rows), rows.size,
-                                 _ptr(out))
+                                 _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_exact_rows rejected its arguments")
-    return out
+    return (out, lse) if want_lse else out
 
 
 def exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, rows=None, nthreads=None, chunk: int = 32):
@@ -262,7 +280,7 @@ def exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, rows=Non
         o = np.empty((rr.size, D), np.float64)
         rc = L.oracle_exact_rows(ctypes.c_void_p(q.ctypes.data + off), ctypes.c_void_p(k.ctypes.data + off),
                                  ctypes.c_void_p(v.ctypes.data + off), S, D, rs, float(sm_scale), _ptr(rr), rr.size,
-                                 _ptr(o))
+                                 _ptr(o), None)
         if rc != 0:
             raise ValueError("oracle_exact_rows rejected its arguments")
         return o

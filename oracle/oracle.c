@@ -185,7 +185,8 @@ int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * Sums inside a tile run in ascending key order. */
 int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                      const uint8_t* v8t, int64_t S_pad, const float* v_scale, int64_t S, int64_t D, float sm_scale,
-                     int64_t T, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16) {
+                     int64_t T, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16,
+                     float* lse_out) {
   if (S < 1 || D < 1 || T < 1 || S_pad < S) return -1;
   const float log2e = 1.44269504088896340736f;
   const float sl2 = sm_scale * log2e;
@@ -231,6 +232,9 @@ int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, c
       }
       m = mnew;
     }
+    /* log-sum-exp of the dequantized scores s_j = t_j ln 2: after the last
+     * tile, l = sum_j 2^(t_j - m), so ln sum_j e^(s_j) = m ln 2 + ln l. */
+    if (lse_out) lse_out[r] = (float)((double)m * 0.69314718055994530942 + log((double)l));
     float denom = 448.0f * l;
     for (int64_t d = 0; d < D; ++d) {
       float val = (o[d] * v_scale[d]) / denom;
@@ -245,7 +249,8 @@ int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, c
 /* Exact attention in double: softmax(q k^T * sm_scale) v, the quantity the
  * method approximates (no quantization, no tiling). */
 int oracle_exact_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S, int64_t D,
-                      int64_t row_stride, double sm_scale, const int64_t* rows, int64_t nrows, double* out) {
+                      int64_t row_stride, double sm_scale, const int64_t* rows, int64_t nrows, double* out,
+                      double* lse_out) {
   if (S < 1 || D < 1) return -1;
   double* s = (double*)malloc((size_t)S * sizeof(double));
   if (!s) return -1;
@@ -262,6 +267,7 @@ int oracle_exact_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
     }
     double den = 0.0;
     for (int64_t j = 0; j < S; ++j) { s[j] = exp(s[j] - mx); den += s[j]; }
+    if (lse_out) lse_out[r] = mx + log(den);   /* ln sum_j e^(s_j) */
     for (int64_t d = 0; d < D; ++d) {
       double num = 0.0;
       for (int64_t j = 0; j < S; ++j) num += s[j] * (double)oracle_bf16_decode(v[j * row_stride + d]);

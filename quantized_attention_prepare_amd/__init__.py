@@ -16,7 +16,7 @@ softmax_scale, ...)):
            return_lse=False, smooth_k=True)
   gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k=True)
   prepare(q, k, v, smooth_k)            -> dict of quantized tensors
-  attn(prepared, sm_scale, out=None)    -> BF16 output
+  attn(prepared, sm_scale, out=None, return_lse=False) -> BF16 output (, lse)
 """
 from __future__ import annotations
 
@@ -83,6 +83,8 @@ def lib():
         L.sage_prepare.restype = ctypes.c_int
         L.sage_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P]
         L.sage_attn.restype = ctypes.c_int
+        L.sage_attn_lse.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P, _P]
+        L.sage_attn_lse.restype = ctypes.c_int
         L.sage_attn_fused.argtypes = [_T, _T, _T, _T, ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_int,
                                       _P, ctypes.c_size_t, _P]
         L.sage_attn_fused.restype = ctypes.c_int
@@ -169,18 +171,24 @@ def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None) ->
     return out
 
 
-def attn(prep: dict, sm_scale: float, out=None, stream=None):
-    """Attention step on prepare()'s output; returns BF16 [B, S, H, 128]."""
+def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = False, lse=None):
+    """Attention step on prepare()'s output; returns BF16 [B, S, H, 128], and with
+    return_lse also the rows' log-sum-exp, float32 [B, H, S] (sage_attn_lse)."""
     import torch
     B, H, Sp, D = prep["q8"].shape
     S = prep["S"]
     if out is None:
         out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=prep["q8"].device)
     to = describe(out)
-    check(lib().sage_attn(_ptr(prep["q8"]), _ptr(prep["q_scale"]), _ptr(prep["k8"]), _ptr(prep["k_scale"]),
-                          _ptr(prep["v8t"]), _ptr(prep["v_scale"]), B, S, H, D, float(sm_scale), ctypes.byref(to),
-                          _stream(stream)))
-    return out
+    args = (_ptr(prep["q8"]), _ptr(prep["q_scale"]), _ptr(prep["k8"]), _ptr(prep["k_scale"]), _ptr(prep["v8t"]),
+            _ptr(prep["v_scale"]), B, S, H, D, float(sm_scale), ctypes.byref(to))
+    if not return_lse:
+        check(lib().sage_attn(*args, _stream(stream)))
+        return out
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=prep["q8"].device)
+    check(lib().sage_attn_lse(*args, _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def fused_workspace_bytes(B: int, S: int, H: int, D: int = HEAD_DIM) -> int:
@@ -192,7 +200,9 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
     """Quantized attention forward (prologue + attention) on one stream.
 
     q, k, v: BF16 [B, S, H, 128] ("NHD") or [B, H, S, 128] ("HND"), equal shapes.
-    Causal attention and return_lse are rejected (NotImplementedError).
+    Causal attention is rejected (NotImplementedError). return_lse=True also
+    returns the rows' log-sum-exp of the dequantized scores, float32 [B, H, S]
+    (an extension: the pages' sageattn rejects it).
     """
     import torch
     if sm_scale is None:
@@ -206,10 +216,11 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
     nws = int(L.sage_fused_workspace_bytes(B, S, H, D))
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if return_lse else None
     check(L.sage_attn_fused(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), int(bool(is_causal)),
-                            float(sm_scale), int(bool(return_lse)), None, int(bool(smooth_k)), _ptr(workspace),
+                            float(sm_scale), int(bool(return_lse)), _ptr(lse), int(bool(smooth_k)), _ptr(workspace),
                             workspace.numel(), _stream(stream)))
-    return out
+    return (out, lse) if return_lse else out
 
 
 def gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k: bool = True):

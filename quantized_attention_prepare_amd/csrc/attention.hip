@@ -60,6 +60,7 @@ constexpr int kQPerWg = 32 * kWaves;
 constexpr int kTileBytes = kKvTile * kHeadDim;   // 16 KB: one K or V tile
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448): folds the P scale into exp2
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferWord3 = 0x00020000;          // raw (untyped) buffer access
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -340,7 +341,8 @@ SAGE_INLINE void pv_tile(WaveState& st, const uint8_t* vbuf, int half, int col) 
 __global__ void __launch_bounds__(kThreads, 2)
 attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, const int8_t* __restrict__ k8,
             const float* __restrict__ k_scale, const uint8_t* __restrict__ v8t, const float* __restrict__ v_scale,
-            int64_t H, int64_t S, int64_t S_pad, int64_t nqt, int64_t nwg, float sl2, Bf16OutView o) {
+            int64_t H, int64_t S, int64_t S_pad, int64_t nqt, int64_t nwg, float sl2, Bf16OutView o,
+            float* __restrict__ lse) {
   // two K and two V tile buffers (indexed by tile & 1), then the workgroup's
   // 128 query rows [query][128 B] (16-byte chunks XOR swizzled by query & 7)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kTileBytes + kQPerWg * kHeadDim];
@@ -457,6 +459,8 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
   const float inv_l = 1.0f / l_tot;
   const int64_t qi = q0 + col;
+  // log-sum-exp of the row's dequantized scores, natural log: l_tot = 448 sum_j 2^(t_j - m)
+  if (lse != nullptr && half == 0 && qi < S) lse[bh * S + qi] = (st.m_run + __log2f(l_tot) - kLog2_448) * kLn2;
   if (qi < S) {
     uint16_t* orow = o.data + b * o.sb + qi * o.ss + h * o.sh;
     const float* vs = v_scale + bh * kHeadDim;
@@ -481,13 +485,13 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                             const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H,
-                            float sm_scale, const Bf16OutView& o, hipStream_t stream) {
+                            float sm_scale, const Bf16OutView& o, float* lse, hipStream_t stream) {
   const int64_t S_pad = padded_len(S);
   const int64_t nqt = (S_pad + kQPerWg - 1) / kQPerWg;
   const int64_t nwg = B * H * nqt;
   const float sl2 = sm_scale * kLog2e;
   hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale, v8t,
-                     v_scale, H, S, S_pad, nqt, nwg, sl2, o);
+                     v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
   return hipGetLastError();
 }
 

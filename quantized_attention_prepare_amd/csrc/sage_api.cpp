@@ -192,15 +192,16 @@ sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_
                       static_cast<hipStream_t>(stream));
 }
 
-sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
-                      const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
-                      float sm_scale, const sage_tensor* o, void* stream) {
+static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                             const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                             float sm_scale, const sage_tensor* o, float* lse, bool want_lse, void* stream) {
   sage_status s;
   if ((s = check_sizes(B, S, H, D))) return s;
   if ((s = check_tensor_args(o, "o"))) return s;
   const bool empty = B * S * H == 0;
   if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "null input pointer");
+  if (want_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "null lse pointer");
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld is not 128", (long long)D);
@@ -209,13 +210,26 @@ sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, 
   const void* ins[] = {q8, q_scale, k8, k_scale, v8t, v_scale};
   for (const void* p : ins)
     if (p && !aligned16(p)) return fail(SAGE_ERR_UNSUPPORTED, "input pointer not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(SAGE_ERR_UNSUPPORTED, "lse not 4-byte aligned");
   if (empty) return ok();
   if ((s = check_device())) return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
   hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, sm_scale, ov,
-                                        static_cast<hipStream_t>(stream));
+                                        want_lse ? lse : nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                      const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                      float sm_scale, const sage_tensor* o, void* stream) {
+  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, o, nullptr, false, stream);
+}
+
+sage_status sage_attn_lse(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                          const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                          float sm_scale, const sage_tensor* o, float* lse, void* stream) {
+  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, o, lse, true, stream);
 }
 
 sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
@@ -231,12 +245,14 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   const bool empty = B * S * H == 0;
   const size_t need = sage_fused_workspace_bytes(B, S, H, q->size[3]);
   if (!empty && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
+  if (return_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "return_lse set but lse is null");
+  if (!return_lse && lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "lse given but return_lse is 0");
   if (is_causal) return fail(SAGE_ERR_UNSUPPORTED, "causal attention is not supported");
-  if (return_lse || lse) return fail(SAGE_ERR_UNSUPPORTED, "log-sum-exp output is not supported");
   if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
       (s = check_tensor_contract(v, "v", q->size)) || (s = check_tensor_contract(o, "o", q->size)))
     return s;
   if (ws && !aligned16(ws)) return fail(SAGE_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(SAGE_ERR_UNSUPPORTED, "lse not 4-byte aligned");
   if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (empty) return ok();
   if ((s = check_device())) return s;
@@ -247,7 +263,8 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
                         ws_bytes, st)))
     return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
-  hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, sm_scale, ov, st);
+  hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, sm_scale, ov,
+                                        return_lse ? lse : nullptr, st);
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -92,12 +92,14 @@ def test_fused_validation_order_on_host():
     bad.size[1] = -1
     assert fused(h, q=bad) == INVALID
     assert fused(h, ws=ctypes.c_void_p(0)) == INVALID
+    # log-sum-exp: the flag and the pointer must agree
+    assert fused(h, lse_flag=1) == INVALID and "lse" in last_error()
+    assert fused(h, lse=ctypes.c_void_p(h.buf().value)) == INVALID and "lse" in last_error()
     # invalid beats unsupported
     assert fused(h, causal=1, sm=float("inf")) == INVALID
     # 2. unsupported contract
     assert fused(h, causal=1) == UNSUPPORTED and "causal" in last_error()
-    assert fused(h, lse_flag=1) == UNSUPPORTED
-    assert fused(h, lse=ctypes.c_void_p(h.buf().value)) == UNSUPPORTED
+    assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value + 2)) == UNSUPPORTED and "lse" in last_error()
     assert fused(h, q=h.tensor(dtype=2), k=h.tensor(dtype=2), v=h.tensor(dtype=2), o=h.tensor(dtype=2)) == UNSUPPORTED
     d64 = (1, 64, 2, 64)
     assert fused(h, q=h.tensor(d64), k=h.tensor(d64), v=h.tensor(d64), o=h.tensor(d64)) == UNSUPPORTED
@@ -112,6 +114,7 @@ def test_fused_validation_order_on_host():
     # 4. with everything valid, the device check is last: no GPU here
     rc = fused(h)
     assert rc == UNSUPPORTED and ("device" in last_error().lower())
+    assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value)) == UNSUPPORTED and "device" in last_error().lower()
 
 
 def test_empty_problem_returns_ok_without_device():
@@ -147,6 +150,17 @@ def test_prepare_and_attn_validation_on_host():
     assert at(D=64) == UNSUPPORTED
     assert at(S=65) == UNSUPPORTED          # o's shape differs from (B, S, H, D)
     assert at() == UNSUPPORTED and "device" in last_error().lower()
+
+    def at_lse(lse, S=64, sm=0.1):
+        return L.sage_attn_lse(*ptrs, 1, S, 2, 128, sm, ctypes.byref(o), lse, None)
+
+    assert at_lse(None) == INVALID and "lse" in last_error()
+    assert at_lse(None, sm=-1.0) == INVALID
+    assert at_lse(ctypes.c_void_p(h.buf().value + 1)) == UNSUPPORTED and "aligned" in last_error()
+    assert at_lse(h.buf()) == UNSUPPORTED and "device" in last_error().lower()
+    z = (1, 0, 2, 128)
+    oz = h.tensor(z)
+    assert L.sage_attn_lse(*ptrs, 1, 0, 2, 128, 0.1, ctypes.byref(oz), None, None) == OK   # empty: nothing to write
 
 
 def test_python_binding_raises_typed_errors():

@@ -177,6 +177,51 @@ def test_attention_ragged(sage, B, S, H, smooth_k):
     compare_attention(f"ragged{B}x{S}x{H}", O, R, E)
 
 
+# ------------------------------------------------------------------ log-sum-exp
+LSE_ABS, LSE_REL = 5e-5, 2e-6   # float sums of l in different orders, hardware exp2/log2
+
+
+def check_lse(name, lse_gpu, lse_orc):
+    d = np.abs(lse_gpu.astype(np.float64) - lse_orc.astype(np.float64))
+    tol = LSE_ABS + LSE_REL * np.abs(lse_orc.astype(np.float64))
+    rec = dict(case=name, lse_max_abs_diff=float(d.max()), lse_max_over_tol=float((d / tol).max()))
+    RESULTS.append(rec)
+    print(json.dumps(rec))
+    assert np.all(d <= tol), rec
+
+
+@pytest.mark.parametrize("B,S,H,smooth_k", [(1, 1, 1, False), (2, 33, 3, True), (1, 300, 2, False),
+                                             (2, 1000, 3, True)])
+def test_lse_ragged(sage, B, S, H, smooth_k):
+    import torch
+    w = synth.custom(B, S, H, smooth_k=smooth_k, base_seed=2500 + S)
+    q, k, v = inputs(w)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    bits, lse_o = oracle.attn(oracle.prepare(q, k, v, smooth_k), w.sm_scale, want_lse=True)
+    assert lse.shape == (B, H, S)
+    check_lse(f"lse{B}x{S}x{H}", lse.cpu().numpy(), lse_o)
+    # asking for the log-sum-exp leaves the output as it is
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), bits) or \
+        oracle.max_abs_rel(oracle.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)),
+                           oracle.bf16_bits_to_f64(bits)) <= MAXABS_TOL
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_lse_workload_rows(sage, name):
+    import torch
+    w = synth.WORKLOADS[name]
+    q, k, v = inputs(w)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, True, w.smooth_k)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, 1024)
+    heads = sorted({(int(b), int(h)) for b, h, _ in rows})
+    prep = oracle.prepare(q, k, v, w.smooth_k, heads=heads)
+    _, lse_o = oracle.attn(prep, w.sm_scale, rows=rows, want_lse=True)
+    g = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check_lse(f"lse_{name}", g, lse_o)
+
+
 def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     import torch
     w = synth.custom(2, 700, 3, smooth_k=True, base_seed=3000)
@@ -185,9 +230,14 @@ def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     f2 = sage.sageattn(q, k, v, smooth_k=True)
     p = sage.prepare(q, k, v, True)
     t = sage.attn(p, w.sm_scale)
+    f3, l3 = sage.sageattn(q, k, v, smooth_k=True, return_lse=True)
+    t2, l2 = sage.attn(p, w.sm_scale, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(f1.view(torch.int16), f2.view(torch.int16))
     assert torch.equal(f1.view(torch.int16), t.view(torch.int16))
+    assert torch.equal(f1.view(torch.int16), f3.view(torch.int16))
+    assert torch.equal(f1.view(torch.int16), t2.view(torch.int16))
+    assert torch.equal(l3.view(torch.int32), l2.view(torch.int32))
 
 
 def test_hnd_layout_and_strided_output_match_nhd(sage):
@@ -219,8 +269,6 @@ def test_unsupported_inputs_raise(sage):
     q = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
         sage.sageattn(q, q, q, is_causal=True)
-    with pytest.raises(NotImplementedError):
-        sage.sageattn(q, q, q, return_lse=True)
     with pytest.raises(NotImplementedError):
         sage.sageattn(q.half(), q.half(), q.half())
     q64 = torch.zeros((1, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
