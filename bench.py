@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C3")
-    ap.add_argument("--others", default="C1,C2,C4,C5", help="comma list of further workloads to report ('' for none)")
+    ap.add_argument("--others", default="C1,C2,C4,C5,C6", help="comma list of further workloads to report ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 512 MiB five times (reference for HBM byte counters)")

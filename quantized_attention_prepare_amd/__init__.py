@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(HERE, "libsage.so")
 
 SAGE_BF16 = 1
 SAGE_OK, SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE_TOO_SMALL, SAGE_ERR_DEVICE = range(5)
-HEAD_DIM = 128
+HEAD_DIM = 128   # the pages' head dim; the library also takes 64
 
 
 class SageTensor(ctypes.Structure):
@@ -172,7 +172,7 @@ def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None) ->
 
 
 def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = False, lse=None):
-    """Attention step on prepare()'s output; returns BF16 [B, S, H, 128], and with
+    """Attention step on prepare()'s output; returns BF16 [B, S, H, D], and with
     return_lse also the rows' log-sum-exp, float32 [B, H, S] (sage_attn_lse)."""
     import torch
     B, H, Sp, D = prep["q8"].shape
@@ -199,7 +199,8 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
              smooth_k: bool = True, out=None, workspace=None, stream=None):
     """Quantized attention forward (prologue + attention) on one stream.
 
-    q, k, v: BF16 [B, S, H, 128] ("NHD") or [B, H, S, 128] ("HND"), equal shapes.
+    q, k, v: BF16 [B, S, H, D] ("NHD") or [B, H, S, D] ("HND"), equal shapes, D = 128
+    (the pages' head dim) or 64.
     Causal attention is rejected (NotImplementedError). return_lse=True also
     returns the rows' log-sum-exp of the dequantized scores, float32 [B, H, S]
     (an extension: the pages' sageattn rejects it).
@@ -224,5 +225,5 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
 
 
 def gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k: bool = True):
-    """BF16 [B, S, H, 128] attention with the quantized forward (NHD layout)."""
+    """BF16 [B, S, H, D] attention with the quantized forward (NHD layout, D = 128 or 64)."""
     return sageattn(query, key, value, "NHD", False, softmax_scale, False, smooth_k)

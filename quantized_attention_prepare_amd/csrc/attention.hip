@@ -33,16 +33,22 @@
 //   query, so the per-query softmax state (m, l, alpha) is lane-local (the two
 //   halves combine with one xor-32 exchange).
 //
-// LDS (80 KB per workgroup): two K tiles [128 keys][128 B] and two V tiles
-// [128 ch][128 B] (tile t in buffer t & 1), filled by buffer loads that write
-// LDS directly, and the workgroup's 128 INT8 query rows. During iteration t
-// the wave reads K(t+1) and V(t) while K(t+2) and V(t+1) are being copied.
+// Head dims 128 and 64 share this code (template parameter D): D/32 score
+// MFMA steps per 32-key block, D/32 output channel blocks; the key tile stays
+// 128 (it is part of the result's definition).
+//
+// LDS (5 * 128 * D bytes per workgroup: 80 KB at D = 128): two K tiles
+// [128 keys][D B] and two V tiles [D ch][128 B] (tile t in buffer t & 1),
+// filled by buffer loads that write LDS directly, and the workgroup's 128 INT8
+// query rows. During iteration t the wave reads K(t+1) and V(t-1) while K(t+2)
+// and V(t) are being copied.
 // Bank layout: gfx950 serves a ds_read_b128 16 lanes at a time from 64 banks of
 // 4 bytes, so 16 consecutive lanes must hit 16 different 16-byte slots of a
-// 256-byte bank row. Rows are 128 bytes (two rows per bank row) and the 16-byte
-// chunk c of row r is stored at c XOR f(r): for V and Q rows f(r) = (r>>1)&7;
-// for K, whose rows are read in the permuted order pi,
-// f(r) = ((r>>1)&3) | ((r>>4)&1)<<2.
+// 256-byte bank row. The 16-byte chunk c of row r is stored at c XOR f(r).
+// 128-byte rows (two per bank row; V always, K and Q at D = 128): for V and Q
+// f(r) = (r>>1)&7, for K, whose rows are read in the permuted order pi,
+// f(r) = ((r>>1)&3) | ((r>>4)&1)<<2. 64-byte rows (four per bank row; K and Q
+// at D = 64): for Q f(r) = (r>>2)&3, for K f(r) = ((r>>2)&1) | ((r>>4)&1)<<1.
 #include "sage_internal.hpp"
 
 namespace sage {
@@ -54,10 +60,23 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
-constexpr int kCopyInstr = 16 / kWaves;   // 1 KB copy instructions per wave per 16 KB tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQPerWg = 32 * kWaves;
-constexpr int kTileBytes = kKvTile * kHeadDim;   // 16 KB: one K or V tile
+
+// Geometry of one head dim D.
+template <int D>
+struct Dim {
+  static constexpr int kTileBytes = kKvTile * D;            // one K or V tile
+  static constexpr int kCopyInstr = kTileBytes / 1024 / kWaves;   // 1 KB copy instructions per wave per tile
+  static constexpr int kSteps = D / 32;                     // 32-channel steps of a score MFMA chain
+  static constexpr int kOBlk = D / 32;                      // 32-channel output blocks
+  static constexpr int kChunks = D / 16;                    // 16-byte chunks in a K or Q row
+  // LDS swizzles (see the header): K rows read in the order pi, Q rows by query
+  static __device__ int fk(int r) {
+    return D == 128 ? (((r >> 1) & 3) | (((r >> 4) & 1) << 2)) : (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
+  }
+  static __device__ int fq(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+};
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448): folds the P scale into exp2
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -67,15 +86,15 @@ constexpr int kBufferWord3 = 0x00020000;          // raw (untyped) buffer access
 #define SAGE_INLINE __device__ __attribute__((always_inline)) inline
 
 // Global -> LDS copies with buffer loads that write LDS directly (16 B per
-// lane). Each wave moves 4 KB of a 16 KB tile: instruction i of wave w fills
-// LDS rows r = 8(4w+i) + lane/8, lane t landing at byte 16 t of that 1 KB. The
-// lane fetches the global chunk that belongs at its swizzled position, chunk
-// (lane % 8) XOR f(r); f(r) depends only on the lane and on (w, i), so each
-// instruction's lane offset is a per-lane constant. One buffer resource per head
-// holds the 64-bit base and the exact byte extent (the hardware bounds-checks
-// every copy); tile and row offsets go in the 32-bit scalar offset and the
-// lane offset in one vector register.
-// K tile t: 128 keys x 128 B, contiguous in k8 (head extent S_pad * 128 B).
+// lane). Each wave moves a quarter of a tile: instruction i of wave w fills the
+// j-th KB of the tile, j = kCopyInstr w + i, lane t landing at byte 16 t of
+// it. The lane fetches the global chunk that belongs at its swizzled position,
+// which depends only on the lane and on j, so each instruction's lane offset
+// is a per-lane constant. One buffer resource per head holds the 64-bit base
+// and the exact byte extent (the hardware bounds-checks every copy); tile and
+// row offsets go in the 32-bit scalar offset and the lane offset in one vector
+// register.
+// K tile t: 128 keys x D B, contiguous in k8 (head extent S_pad * D B).
 // The LDS destination goes through an empty asm so that its per-instruction
 // addresses are formed next to each copy instead of being precomputed for
 // every buffer and kept live in scalar registers across the loop.
@@ -84,24 +103,27 @@ SAGE_INLINE uint8_t* opaque_lds(uint8_t* dst) {
   asm volatile("" : "+s"(a));
   return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t)a;
 }
-SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t, const uint32_t (&lane_off)[kCopyInstr],
-                        int wave) {
+template <int D>
+SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t,
+                        const uint32_t (&lane_off)[Dim<D>::kCopyInstr], int wave) {
+  constexpr int C = Dim<D>::kCopyInstr;
   dst = opaque_lds(dst);
 #pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(dst + 1024 * (kCopyInstr * wave + i)), 16, lane_off[i],
-                                             (uint32_t)t * kTileBytes + 1024u * (kCopyInstr * wave + i), 0, 0);
+  for (int i = 0; i < C; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(dst + 1024 * (C * wave + i)), 16, lane_off[i],
+                                             (uint32_t)t * Dim<D>::kTileBytes + 1024u * (C * wave + i), 0, 0);
 }
-// V tile t: 128 channels x 128 keys; channel rows are S_pad bytes apart in v8t
-// (head extent 128 * S_pad B).
+// V tile t: D channels x 128 keys; channel rows are S_pad bytes apart in v8t
+// (head extent D * S_pad B); each KB is 8 channel rows.
+template <int D>
 SAGE_INLINE void load_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rv, int t, uint32_t S_pad,
-                        const uint32_t (&lane_off)[kCopyInstr], int wave) {
+                        const uint32_t (&lane_off)[Dim<D>::kCopyInstr], int wave) {
+  constexpr int C = Dim<D>::kCopyInstr;
   dst = opaque_lds(dst);
 #pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(dst + 1024 * (kCopyInstr * wave + i)), 16, lane_off[i],
-                                             (uint32_t)t * kKvTile + (uint32_t)(8 * (kCopyInstr * wave + i)) * S_pad,
-                                             0, 0);
+  for (int i = 0; i < C; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(dst + 1024 * (C * wave + i)), 16, lane_off[i],
+                                             (uint32_t)t * kKvTile + (uint32_t)(8 * (C * wave + i)) * S_pad, 0, 0);
 }
 
 SAGE_INLINE uint32_t pack_bf16x2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
@@ -116,8 +138,9 @@ SAGE_INLINE float max_xor32(float v) {
 }
 
 // Per-wave online-softmax state and output accumulators.
+template <int D>
 struct WaveState {
-  v16f oacc[4];   // O^T blocks: channels 32*d + 8(v/4) + 4h + v%4 of this lane's query
+  v16f oacc[D / 32];   // O^T blocks: channels 32*d + 8(v/4) + 4h + v%4 of this lane's query
   v8i pk[2];      // FP8 probabilities of the tile whose PV is next (two 64-key halves)
   float m_run;    // running max (log2 units)
   float l_run;    // this lane-half's share of 448 * sum p
@@ -126,16 +149,17 @@ struct WaveState {
 // INT8 scores S^T = K . Q^T of one tile into sacc: row pi(col) of each 32-key
 // block, channels 32s + 16h .. +15; the four score blocks are independent
 // MFMAs.
+template <int D>
 SAGE_INLINE void qk_tile(v16i (&sacc)[4], const uint8_t* kbuf, const uint8_t* qrow, int half, int col, int prow) {
-  const uint8_t* krow = kbuf + prow * kHeadDim;
-  const int fk = ((prow >> 1) & 3) | (((prow >> 4) & 1) << 2);   // f(32 kb + prow) for every kb
-  const int fq = (col >> 1) & 7;
+  const uint8_t* krow = kbuf + prow * D;
+  const int fk = Dim<D>::fk(prow);   // f(32 kb + prow) for every kb
+  const int fq = Dim<D>::fq(col);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < Dim<D>::kSteps; ++s) {
     const v4i qb = *reinterpret_cast<const v4i*>(qrow + (((2 * s + half) ^ fq) * 16));
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const v4i a = *reinterpret_cast<const v4i*>(krow + 32 * kb * kHeadDim + (((2 * s + half) ^ fk) * 16));
+      const v4i a = *reinterpret_cast<const v4i*>(krow + 32 * kb * D + (((2 * s + half) ^ fk) * 16));
       if (s == 0) {
         const v16i z = {};
         sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb, z, 0, 0, 0);
@@ -206,6 +230,7 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
 //   slots 9-24  the INT8 score MFMAs of the next tile, with the exp2 of blocks
 //               2 and 3, l, and the rescale of O (the previous PV is complete by
 //               then).
+// At D = 64 there are four PV and eight score MFMAs, two exp2 groups per slot.
 // The LDS operands of each MFMA are read one slot ahead. kHasPrev is false for
 // the first tile. cblk[kb] = (q_scale * k_scale) * sm_scale * log2 e of the
 // tile's 32-key blocks. nvalid < 128 marks a ragged last tile: padded keys'
@@ -213,15 +238,15 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
 // made only of padding come with cblk = +inf (probability exactly 0), and in
 // the partly padded block the padded keys' probability, which only matters for
 // l (their V codes are 0), is subtracted from l afterwards.
-template <bool kHasPrev>
-SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], const float (&cblk)[4], int nvalid,
-                                const uint8_t* vbuf_prev, const uint8_t* kbuf_next, const uint8_t* qrow, int half,
-                                int col, int prow) {
+template <int D, bool kHasPrev>
+SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4], const float (&cblk)[4],
+                                int nvalid, const uint8_t* vbuf_prev, const uint8_t* kbuf_next, const uint8_t* qrow,
+                                int half, int col, int prow) {
   const int kbase = 16 * half;
-  const int fk = ((prow >> 1) & 3) | (((prow >> 4) & 1) << 2);   // K swizzle of rows 32 kb + prow
-  const int fq = (col >> 1) & 7;                                 // Q swizzle of row col
-  const int fv = (col >> 1) & 7;                                 // V swizzle of rows 32 d + col
-  const uint8_t* krow = kbuf_next + prow * kHeadDim;
+  const int fk = Dim<D>::fk(prow);   // K swizzle of rows 32 kb + prow
+  const int fq = Dim<D>::fq(col);    // Q swizzle of row col
+  const int fv = (col >> 1) & 7;     // V swizzle of rows 32 d + col
+  const uint8_t* krow = kbuf_next + prow * D;
   // ---- slot 0: first V operand; tail masking; max of blocks 0, 1
   v8i vop;
   if (kHasPrev) vop = v_operand(vbuf_prev, 0, 0, half, col, fv);
@@ -255,6 +280,20 @@ SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], 
   float m_new, alpha, moff;
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #define SAGE_EXP(KB_, G_) exp_group(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
+  v4i qop, kop;
+#define SAGE_L_UPDATE()                                                                               \
+  {                                                                                                   \
+    float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                   \
+    if (nvalid < kKvTile && (nvalid & 31)) {                                                          \
+      const int kbp = nvalid >> 5; /* the partly padded block */                                      \
+      const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - nvalid));                              \
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, cblk[kbp], -moff));   \
+      if (nmask > 0) psum -= (float)nmask * pm;                                                       \
+    }                                                                                                 \
+    st.l_run = alpha * st.l_run + psum;                                                               \
+    st.m_run = m_new;                                                                                 \
+  }
+  if constexpr (D == 128) {
   SAGE_PV_SLOT(0, 0, 0, 1, tmax = fmaxf(tmax, fmaxf(block_max(sc[2], cblk[2]), block_max(sc[3], cblk[3]))))
   SAGE_PV_SLOT(0, 1, 0, 2, {
     tmax = max_xor32(tmax);
@@ -268,26 +307,43 @@ SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], 
   SAGE_PV_SLOT(1, 0, 1, 1, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
   SAGE_PV_SLOT(1, 1, 1, 2, { SAGE_EXP(0, 2); SAGE_EXP(0, 3); })
   SAGE_PV_SLOT(1, 2, 1, 3, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
-  v4i qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
-  v4i kop;
+  qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
   SAGE_PV_SLOT(1, 3, -1, 0, {
     kop = *reinterpret_cast<const v4i*>(krow + (((0 + half) ^ fk) * 16));
     SAGE_EXP(1, 2);
     SAGE_EXP(1, 3);
   })
+  } else {
+  SAGE_PV_SLOT(0, 0, 0, 1, tmax = fmaxf(tmax, fmaxf(block_max(sc[2], cblk[2]), block_max(sc[3], cblk[3]))))
+  SAGE_PV_SLOT(0, 1, 1, 0, {
+    tmax = max_xor32(tmax);
+    m_new = fmaxf(st.m_run, tmax);
+    alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
+    moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
+  })
+  // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
+  SAGE_PV_SLOT(1, 0, 1, 1, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
+  qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
+  SAGE_PV_SLOT(1, 1, -1, 0, {
+    kop = *reinterpret_cast<const v4i*>(krow + (((0 + half) ^ fk) * 16));
+    SAGE_EXP(0, 2);
+    SAGE_EXP(0, 3);
+  })
+  }
 #undef SAGE_PV_SLOT
-  // ---- slots 9-24: score MFMAs of the next tile (s outer, kb inner)
+  // ---- score MFMAs of the next tile (s outer, kb inner)
 #define SAGE_QK_SLOT(S_, KB_, NS_, NKB_, WORK_)                                                         \
   {                                                                                                      \
     const v16i z = {};                                                                                   \
     snext[KB_] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop, (S_) == 0 ? z : snext[KB_], 0, 0, 0);   \
     if ((NS_) >= 0) {                                                                                    \
       if ((NS_) != (S_)) qop = *reinterpret_cast<const v4i*>(qrow + (((2 * (NS_) + half) ^ fq) * 16));   \
-      kop = *reinterpret_cast<const v4i*>(krow + 32 * (NKB_) * kHeadDim + (((2 * (NS_) + half) ^ fk) * 16)); \
+      kop = *reinterpret_cast<const v4i*>(krow + 32 * (NKB_) * D + (((2 * (NS_) + half) ^ fk) * 16));  \
     }                                                                                                    \
     WORK_;                                                                                               \
     SAGE_FENCE();                                                                                        \
   }
+  if constexpr (D == 128) {
   SAGE_QK_SLOT(0, 0, 0, 1, SAGE_EXP(2, 0))
   SAGE_QK_SLOT(0, 1, 0, 2, (void)0)
   SAGE_QK_SLOT(0, 2, 0, 3, SAGE_EXP(2, 1))
@@ -303,17 +359,19 @@ SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], 
   SAGE_QK_SLOT(3, 0, 3, 1, SAGE_EXP(3, 2))
   SAGE_QK_SLOT(3, 1, 3, 2, (void)0)
   SAGE_QK_SLOT(3, 2, 3, 3, SAGE_EXP(3, 3))
-  SAGE_QK_SLOT(3, 3, -1, 0, {
-    float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    if (nvalid < kKvTile && (nvalid & 31)) {
-      const int kbp = nvalid >> 5;   // the partly padded block
-      const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - nvalid));
-      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, cblk[kbp], -moff));
-      if (nmask > 0) psum -= (float)nmask * pm;
-    }
-    st.l_run = alpha * st.l_run + psum;
-    st.m_run = m_new;
-  })
+  SAGE_QK_SLOT(3, 3, -1, 0, SAGE_L_UPDATE())
+  } else {
+  SAGE_QK_SLOT(0, 0, 0, 1, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
+  SAGE_QK_SLOT(0, 1, 0, 2, { SAGE_EXP(1, 2); SAGE_EXP(1, 3); })
+  // pk[1] of the previous tile has been handed to its MFMAs as well
+  SAGE_QK_SLOT(0, 2, 0, 3, { SAGE_EXP(2, 0); SAGE_EXP(2, 1); })
+  SAGE_QK_SLOT(0, 3, 1, 0, { SAGE_EXP(2, 2); SAGE_EXP(2, 3); })
+  SAGE_QK_SLOT(1, 0, 1, 1, { SAGE_EXP(3, 0); SAGE_EXP(3, 1); })
+  SAGE_QK_SLOT(1, 1, 1, 2, { SAGE_EXP(3, 2); SAGE_EXP(3, 3); })
+  SAGE_QK_SLOT(1, 2, 1, 3, SAGE_L_UPDATE())
+  SAGE_QK_SLOT(1, 3, -1, 0, (void)0)
+  }
+#undef SAGE_L_UPDATE
 #undef SAGE_QK_SLOT
 #undef SAGE_EXP
   // Rescale O to the new maximum (the previous tile's PV has completed by
@@ -321,43 +379,49 @@ SAGE_INLINE void tile_iteration(WaveState& st, v16i (&sc)[4], v16i (&snext)[4], 
   // one, and after the first tiles that is the usual case.
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < Dim<D>::kOBlk; ++d)
 #pragma unroll
       for (int v = 0; v < 16; ++v) st.oacc[d][v] *= alpha;
   }
 }
 
 // PV of the last tile, after the loop.
-SAGE_INLINE void pv_tile(WaveState& st, const uint8_t* vbuf, int half, int col) {
+template <int D>
+SAGE_INLINE void pv_tile(WaveState<D>& st, const uint8_t* vbuf, int half, int col) {
   const int fv = (col >> 1) & 7;
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < Dim<D>::kOBlk; ++d)
       st.oacc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_operand(vbuf, kc, d, half, col, fv), st.pk[kc],
                                                                    st.oacc[d], 0, 0, 0, 0, 0, 0);
 }
 
+template <int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, const int8_t* __restrict__ k8,
             const float* __restrict__ k_scale, const uint8_t* __restrict__ v8t, const float* __restrict__ v_scale,
             int64_t H, int64_t S, int64_t S_pad, int64_t nqt, int64_t nwg, float sl2, Bf16OutView o,
             float* __restrict__ lse) {
+  using Dm = Dim<D>;
+  constexpr int C = Dm::kCopyInstr, TB = Dm::kTileBytes;
   // two K and two V tile buffers (indexed by tile & 1), then the workgroup's
-  // 128 query rows [query][128 B] (16-byte chunks XOR swizzled by query & 7)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kTileBytes + kQPerWg * kHeadDim];
-#define KBUF(i) (lds + (i) * kTileBytes)
-#define VBUF(i) (lds + (2 + (i)) * kTileBytes)
+  // 128 query rows [query][D B] (16-byte chunks XOR swizzled by fq(query))
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TB + kQPerWg * D];
+#define KBUF(i) (lds + (i) * TB)
+#define VBUF(i) (lds + (2 + (i)) * TB)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  // copy chunk of this lane: (lane % 8) XOR f(row) for row = 8 j + lane / 8, j = 4 wave + i
-  uint32_t k_lane_off[kCopyInstr];
+  // K copy: the j-th KB (j = C wave + i) holds rows (1024 / D) j + lane / (D/16),
+  // lane landing at chunk lane % (D/16); it fetches global chunk
+  // (lane % (D/16)) XOR fk(row)
+  uint32_t k_lane_off[C];
 #pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i) {
-    const int j = kCopyInstr * wave + i;
-    k_lane_off[i] =
-        (uint32_t)((lane >> 3) * kHeadDim + (((lane & 7) ^ (((lane >> 4) & 3) | (((j >> 1) & 1) << 2))) * 16));
+  for (int i = 0; i < C; ++i) {
+    const int j = C * wave + i;
+    const int row = (1024 / D) * j + lane / Dm::kChunks, slot = lane % Dm::kChunks;
+    k_lane_off[i] = (uint32_t)((lane / Dm::kChunks) * D + ((slot ^ Dm::fk(row)) * 16));
   }
 
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
@@ -373,35 +437,40 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const bool active = q0 < S_pad;                // the last workgroup may reach past S_pad
   const uint32_t spad32 = (uint32_t)S_pad;       // 128 S_pad < 2^32 (host check)
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(k8 + bh * S_pad * kHeadDim), 0, (int)(spad32 * kHeadDim), kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k8 + bh * S_pad * D), 0, (int)(spad32 * D), kBufferWord3);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(v8t + bh * kHeadDim * S_pad), 0, (int)(spad32 * kHeadDim), kBufferWord3);
-  uint32_t v_lane_off[kCopyInstr];
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v8t + bh * D * S_pad), 0, (int)(spad32 * D), kBufferWord3);
+  // V copy: the j-th KB holds channel rows 8 j + lane / 8 (128 B each); the
+  // swizzle (row >> 1) & 7 = ((lane >> 4) & 3) | ((j & 1) << 2), and j & 1 =
+  // i & 1 because C is even
+  static_assert(C % 2 == 0, "V copy swizzle assumes an even number of copies per wave");
+  uint32_t v_lane_off[C];
 #pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i)
+  for (int i = 0; i < C; ++i)
     v_lane_off[i] = (uint32_t)(lane >> 3) * spad32 + (uint32_t)(((lane & 7) ^ (((lane >> 4) & 3) | ((i & 1) << 2))) * 16);
   const float* ks = k_scale + bh * (S_pad / kQBlock);
   const float qs = active ? q_scale[bh * (S_pad / kQBlock) + q0 / kQBlock] : 0.0f;
 
   // This wave's 32 query rows go to LDS once (zeros past S_pad); the score
   // MFMAs read their B operand from there.
-  uint8_t* qlds = lds + 4 * kTileBytes + 32 * wave * kHeadDim;
+  uint8_t* qlds = lds + 4 * TB + 32 * wave * D;
   {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * i + (lane >> 3), c = lane & 7;   // row r of the wave, 16-byte chunk c
+    for (int i = 0; i < D / 32; ++i) {
+      // row r of the wave, 16-byte chunk c
+      const int r = (1024 / D) * i + lane / Dm::kChunks, c = lane % Dm::kChunks;
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (active) val = *reinterpret_cast<const uint4*>(q8 + (bh * S_pad + q0 + r) * kHeadDim + c * 16);
-      *reinterpret_cast<uint4*>(qlds + r * kHeadDim + ((c ^ ((r >> 1) & 7)) * 16)) = val;
+      if (active) val = *reinterpret_cast<const uint4*>(q8 + (bh * S_pad + q0 + r) * D + c * 16);
+      *reinterpret_cast<uint4*>(qlds + r * D + ((c ^ Dm::fq(r)) * 16)) = val;
     }
   }
-  const uint8_t* qrow = qlds + col * kHeadDim;
+  const uint8_t* qrow = qlds + col * D;
   // A-operand row of the score MFMA fed by this lane: key pi(col) of a 32-key block
   const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
 
-  WaveState st;
+  WaveState<D> st;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < Dm::kOBlk; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) st.oacc[d][v] = 0.0f;
 #pragma unroll
@@ -415,12 +484,12 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const int last_valid = (int)(S - (int64_t)(ntiles - 1) * kKvTile);   // valid keys in the last tile (1..128)
 
   // K(0), K(1) in; scores of tile 0.
-  load_k(KBUF(0), rk, 0, k_lane_off, wave);
-  if (ntiles > 1) load_k(KBUF(1), rk, 1, k_lane_off, wave);
+  load_k<D>(KBUF(0), rk, 0, k_lane_off, wave);
+  if (ntiles > 1) load_k<D>(KBUF(1), rk, 1, k_lane_off, wave);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v16i sa[4], sb[4];   // scores of the current and the next tile; they swap roles every iteration
-  qk_tile(sa, KBUF(0), qrow, half, col, prow);
+  qk_tile<D>(sa, KBUF(0), qrow, half, col, prow);
   float4 ksv = *reinterpret_cast<const float4*>(ks);   // k_scale of the four blocks of the current tile
 
   // Iteration t: PV of tile t-1, softmax of tile t, scores of tile t+1. On
@@ -432,15 +501,15 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
     const int t_ = (T_);                                                                                       \
     __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                      \
     __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                  \
-    if (t_ + 2 < ntiles) load_k(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                   \
-    load_v(VBUF(t_ & 1), rv, t_, spad32, v_lane_off, wave);                                                    \
+    if (t_ + 2 < ntiles) load_k<D>(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                \
+    load_v<D>(VBUF(t_ & 1), rv, t_, spad32, v_lane_off, wave);                                                 \
     const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                                \
     const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                         \
     float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block made only of padding */        \
     for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nvalid ? INFINITY : (qs * kss[kb]) * sl2;             \
     if (t_ + 1 < ntiles) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                            \
-    tile_iteration<HAS_PREV_>(st, CUR_, NEXT_, cblk, nvalid, VBUF((t_ + 1) & 1), KBUF((t_ + 1) & 1), qrow,     \
-                              half, col, prow);                                                                \
+    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, nvalid, VBUF((t_ + 1) & 1), KBUF((t_ + 1) & 1), qrow,  \
+                                 half, col, prow);                                                             \
   }
   SAGE_ITERATION(0, false, sa, sb)
   int t = 1;
@@ -453,7 +522,7 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // PV of the last tile
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  pv_tile(st, VBUF((ntiles - 1) & 1), half, col);
+  pv_tile<D>(st, VBUF((ntiles - 1) & 1), half, col);
 
   // ---- epilogue: O = o * v_scale / (448 l)
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
@@ -463,9 +532,9 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   if (lse != nullptr && half == 0 && qi < S) lse[bh * S + qi] = (st.m_run + __log2f(l_tot) - kLog2_448) * kLn2;
   if (qi < S) {
     uint16_t* orow = o.data + b * o.sb + qi * o.ss + h * o.sh;
-    const float* vs = v_scale + bh * kHeadDim;
+    const float* vs = v_scale + bh * D;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < Dm::kOBlk; ++d) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int ch = 32 * d + 8 * a + 4 * half;
@@ -484,14 +553,18 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 }  // namespace
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
-                            const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H,
+                            const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                             float sm_scale, const Bf16OutView& o, float* lse, hipStream_t stream) {
   const int64_t S_pad = padded_len(S);
   const int64_t nqt = (S_pad + kQPerWg - 1) / kQPerWg;
   const int64_t nwg = B * H * nqt;
   const float sl2 = sm_scale * kLog2e;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale, v8t,
-                     v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
+  if (D == 64)
+    hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale,
+                       v8t, v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
+  else
+    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale,
+                       v8t, v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Prologue of the quantized attention forward on gfx950: BF16 Q/K -> INT8 per
 // 32-row block, BF16 V -> OCP FP8 E4M3 per channel, optional smooth_k (the
-// per-channel key mean, summed in fp64, subtracted from K first).
+// per-channel key mean, summed in fp64, subtracted from K first). Head dims 128
+// and 64 (one template; a 64-channel row is covered by 8 lanes instead of 16).
 //
 // Method: kernels-community issue "aiter-sage-attention" (section "The
 // kernel": Q/K per 32-row block, V per channel) and the SageAttention-RDNA4
@@ -47,22 +48,35 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-// Quantize one 32-row x 128-channel block held as x[i*8+e] = element
-// (row 4i + lane/16, channel 8*(lane%16) + e); invalid rows hold 0.
+// Lane geometry of one wave over a 32-row block of D channels: lane (c, g),
+// c = lane % L, g = lane / L, holds channels 8c .. 8c+7 of rows G*i + g,
+// i = 0 .. I-1 (L lanes per row, G row groups, I rows per lane).
+template <int D>
+struct Geo {
+  static constexpr int L = D / 8;
+  static constexpr int G = 64 / L;
+  static constexpr int I = 32 / G;
+};
+
+// Quantize one 32-row x D-channel block held as x[i*8+e] = element
+// (row G*i + g, channel 8c + e); invalid rows hold 0.
 // Writes the 32 rows of codes and the block's scale.
-__device__ inline void quant_block_store(const float (&x)[64], int8_t* dst_rows, float* scale_out, int lane) {
+template <int D>
+__device__ inline void quant_block_store(const float (&x)[8 * Geo<D>::I], int8_t* dst_rows, float* scale_out,
+                                         int lane) {
+  using Gm = Geo<D>;
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(x[i]));
+  for (int i = 0; i < 8 * Gm::I; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
   float scale = 0.0f, inv = 0.0f;
   if (a != 0.0f) {
     scale = a / 127.0f;   // correctly rounded IEEE division
     inv = 127.0f / a;
   }
-  const int c = lane & 15, g = lane >> 4;
+  const int c = lane % Gm::L, g = lane / Gm::L;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < Gm::I; ++i) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -71,21 +85,23 @@ __device__ inline void quant_block_store(const float (&x)[64], int8_t* dst_rows,
       uint32_t byte = (uint32_t)(int32_t)r & 0xFFu;
       if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
     }
-    *reinterpret_cast<uint2*>(dst_rows + (int64_t)(4 * i + g) * kHeadDim + 8 * c) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(dst_rows + (int64_t)(Gm::G * i + g) * D + 8 * c) = make_uint2(lo, hi);
   }
   if (lane == 0) *scale_out = scale;
 }
 
+template <int D>
 __global__ void __launch_bounds__(kThreads)
 stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int chunks_per_wg,
              int64_t nparts, int smooth_k, int8_t* __restrict__ q8, float* __restrict__ q_scale,
              int8_t* __restrict__ k8, float* __restrict__ k_scale, double* __restrict__ ksum_part,
              float* __restrict__ vmax_part) {
+  using Gm = Geo<D>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = (int64_t)blockIdx.x / nparts, part = (int64_t)blockIdx.x % nparts;
   const int64_t b = bh / H, h = bh % H;
   const int64_t nchunks = S_pad / kChunk;
-  const int c = lane & 15, g = lane >> 4;
+  const int c = lane % Gm::L, g = lane / Gm::L;
   const uint16_t* qb = q.data + b * q.sb + h * q.sh + 8 * c;
   const uint16_t* kb = k.data + b * k.sb + h * k.sh + 8 * c;
   const uint16_t* vb = v.data + b * v.sb + h * v.sh + 8 * c;
@@ -98,34 +114,34 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   for (int64_t ch = part * chunks_per_wg; ch < nchunks && ch < (part + 1) * chunks_per_wg; ++ch) {
     const int64_t r0 = ch * kChunk + 32 * wave;   // first row of this wave's block
     const int64_t blk = r0 / kQBlock;
-    float x[64];
+    float x[8 * Gm::I];
     // Q: quantize the block
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = r0 + 4 * i + g;
+    for (int i = 0; i < Gm::I; ++i) {
+      int64_t row = r0 + Gm::G * i + g;
       Row16 r = row < S ? load16(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
       unpack(r, &x[i * 8]);
     }
-    quant_block_store(x, q8 + (bh * S_pad + r0) * kHeadDim, q_scale + bh * (S_pad / kQBlock) + blk, lane);
+    quant_block_store<D>(x, q8 + (bh * S_pad + r0) * D, q_scale + bh * (S_pad / kQBlock) + blk, lane);
     // K: statistics (smooth_k) or quantize right away
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = r0 + 4 * i + g;
+    for (int i = 0; i < Gm::I; ++i) {
+      int64_t row = r0 + Gm::G * i + g;
       Row16 r = row < S ? load16(kb + row * k.ss) : Row16{{0, 0, 0, 0}};
       unpack(r, &x[i * 8]);
     }
     if (smooth_k) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < Gm::I; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) ksum[e] += (double)x[i * 8 + e];
     } else {
-      quant_block_store(x, k8 + (bh * S_pad + r0) * kHeadDim, k_scale + bh * (S_pad / kQBlock) + blk, lane);
+      quant_block_store<D>(x, k8 + (bh * S_pad + r0) * D, k_scale + bh * (S_pad / kQBlock) + blk, lane);
     }
     // V: channel absolute maxima
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = r0 + 4 * i + g;
+    for (int i = 0; i < Gm::I; ++i) {
+      int64_t row = r0 + Gm::G * i + g;
       Row16 r = row < S ? load16(vb + row * v.ss) : Row16{{0, 0, 0, 0}};
       float y[8];
       unpack(r, y);
@@ -134,27 +150,28 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
     }
   }
 
-  // Fold the four row groups of the wave (lanes c, c+16, c+32, c+48), then the
+  // Fold the row groups of the wave (lanes c, c + L, c + 2L, ...), then the
   // four waves, always in the same order.
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ksum[e] += __shfl_xor(ksum[e], 16, 64);
-    ksum[e] += __shfl_xor(ksum[e], 32, 64);
-    vmax[e] = fmaxf(vmax[e], __shfl_xor(vmax[e], 16, 64));
-    vmax[e] = fmaxf(vmax[e], __shfl_xor(vmax[e], 32, 64));
+#pragma unroll
+    for (int m = Gm::L; m < 64; m <<= 1) {
+      ksum[e] += __shfl_xor(ksum[e], m, 64);
+      vmax[e] = fmaxf(vmax[e], __shfl_xor(vmax[e], m, 64));
+    }
   }
-  __shared__ double s_sum[4][kHeadDim];
-  __shared__ float s_max[4][kHeadDim];
+  __shared__ double s_sum[4][D];
+  __shared__ float s_max[4][D];
   if (g == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) { s_sum[wave][8 * c + e] = ksum[e]; s_max[wave][8 * c + e] = vmax[e]; }
   }
   __syncthreads();
-  if (tid < kHeadDim) {
+  if (tid < D) {
     double s = ((s_sum[0][tid] + s_sum[1][tid]) + s_sum[2][tid]) + s_sum[3][tid];
     float m = fmaxf(fmaxf(s_max[0][tid], s_max[1][tid]), fmaxf(s_max[2][tid], s_max[3][tid]));
-    ksum_part[(bh * nparts + part) * kHeadDim + tid] = s;
-    vmax_part[(bh * nparts + part) * kHeadDim + tid] = m;
+    ksum_part[(bh * nparts + part) * D + tid] = s;
+    vmax_part[(bh * nparts + part) * D + tid] = m;
   }
 }
 
@@ -164,21 +181,22 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 // every run.
 constexpr int kFinalizeSlices = 8;
 
-__global__ void __launch_bounds__(kHeadDim * kFinalizeSlices)
+template <int D>
+__global__ void __launch_bounds__(D * kFinalizeSlices)
 finalize_kernel(int64_t S, int64_t nparts, int smooth_k, const double* __restrict__ ksum_part,
                 const float* __restrict__ vmax_part, float* __restrict__ kmean, float* __restrict__ vinv,
                 float* __restrict__ v_scale, float* __restrict__ k_mean_out) {
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x % kHeadDim, j = threadIdx.x / kHeadDim;
+  const int d = threadIdx.x % D, j = threadIdx.x / D;
   double s = 0.0;
   float a = 0.0f;
 #pragma unroll 8
   for (int64_t p = j; p < nparts; p += kFinalizeSlices) {
-    s += ksum_part[(bh * nparts + p) * kHeadDim + d];
-    a = fmaxf(a, vmax_part[(bh * nparts + p) * kHeadDim + d]);
+    s += ksum_part[(bh * nparts + p) * D + d];
+    a = fmaxf(a, vmax_part[(bh * nparts + p) * D + d]);
   }
-  __shared__ double s_sum[kFinalizeSlices][kHeadDim];
-  __shared__ float s_max[kFinalizeSlices][kHeadDim];
+  __shared__ double s_sum[kFinalizeSlices][D];
+  __shared__ float s_max[kFinalizeSlices][D];
   s_sum[j][d] = s;
   s_max[j][d] = a;
   __syncthreads();
@@ -189,34 +207,36 @@ finalize_kernel(int64_t S, int64_t nparts, int smooth_k, const double* __restric
     a = fmaxf(a, s_max[i][d]);
   }
   float km = smooth_k ? (float)(s / (double)S) : 0.0f;
-  kmean[bh * kHeadDim + d] = km;
-  if (k_mean_out) k_mean_out[bh * kHeadDim + d] = km;
-  v_scale[bh * kHeadDim + d] = a == 0.0f ? 0.0f : a / 448.0f;
-  vinv[bh * kHeadDim + d] = a == 0.0f ? 0.0f : 448.0f / a;
+  kmean[bh * D + d] = km;
+  if (k_mean_out) k_mean_out[bh * D + d] = km;
+  v_scale[bh * D + d] = a == 0.0f ? 0.0f : a / 448.0f;
+  vinv[bh * D + d] = a == 0.0f ? 0.0f : 448.0f / a;
 }
 
+template <int D>
 __global__ void __launch_bounds__(kThreads)
 quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int smooth_k,
              const float* __restrict__ kmean, const float* __restrict__ vinv, int8_t* __restrict__ k8,
              float* __restrict__ k_scale, uint8_t* __restrict__ v8t) {
-  __shared__ uint32_t tile[kHeadDim * kVTileStride / 4];   // [channel][row] codes, 132-byte rows
+  using Gm = Geo<D>;
+  __shared__ uint32_t tile[D * kVTileStride / 4];   // [channel][row] codes, 132-byte rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nchunks = S_pad / kChunk;
   const int64_t id = (int64_t)gridDim.x - 1 - (int64_t)blockIdx.x;   // reverse of the stats order
   const int64_t bh = id / nchunks, ch = id % nchunks;
   const int64_t b = bh / H, h = bh % H;
-  const int c = lane & 15, g = lane >> 4;
+  const int c = lane % Gm::L, g = lane / Gm::L;
 
   if (smooth_k) {
     const int64_t r0 = ch * kChunk + 32 * wave;
     const uint16_t* kb = k.data + b * k.sb + h * k.sh + 8 * c;
     float km[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) km[e] = kmean[bh * kHeadDim + 8 * c + e];
-    float x[64];
+    for (int e = 0; e < 8; ++e) km[e] = kmean[bh * D + 8 * c + e];
+    float x[8 * Gm::I];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = r0 + 4 * i + g;
+    for (int i = 0; i < Gm::I; ++i) {
+      int64_t row = r0 + Gm::G * i + g;
       float y[8];
       if (row < S) {
         unpack(load16(kb + row * k.ss), y);
@@ -227,20 +247,21 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
         for (int e = 0; e < 8; ++e) x[i * 8 + e] = 0.0f;   // padding rows stay zero
       }
     }
-    quant_block_store(x, k8 + (bh * S_pad + r0) * kHeadDim, k_scale + bh * (S_pad / kQBlock) + r0 / kQBlock, lane);
+    quant_block_store<D>(x, k8 + (bh * S_pad + r0) * D, k_scale + bh * (S_pad / kQBlock) + r0 / kQBlock, lane);
   }
 
-  // V: lane (c, g) of wave w converts rows 32w + 4g + j and 32w + 16 + 4g + j
-  // (j = 0..3) of channels 8c..8c+7, so each lane owns four consecutive rows
-  // per channel and can write them to the transposed tile as one dword.
+  // V: lane (c, g) of wave w converts rows 32w + 4G*half + 4g + j (j = 0..3,
+  // half = 0 .. 8/G - 1) of channels 8c..8c+7, so each lane owns four
+  // consecutive rows per channel and can write them to the transposed tile as
+  // one dword.
   {
     const uint16_t* vb = v.data + b * v.sb + h * v.sh + 8 * c;
     float inv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) inv[e] = vinv[bh * kHeadDim + 8 * c + e];
+    for (int e = 0; e < 8; ++e) inv[e] = vinv[bh * D + 8 * c + e];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int rl = 32 * wave + 16 * half + 4 * g;   // local row of j = 0
+    for (int half = 0; half < 8 / Gm::G; ++half) {
+      const int rl = 32 * wave + 4 * Gm::G * half + 4 * g;   // local row of j = 0
       uint32_t codes[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) codes[e] = 0;
@@ -266,10 +287,10 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
     }
   }
   __syncthreads();
-  // write 128 channel rows x 128 keys; thread t moves 16-byte pieces
-  uint8_t* vdst = v8t + bh * kHeadDim * S_pad + ch * kChunk;
+  // write D channel rows x 128 keys; thread t moves 16-byte pieces
+  uint8_t* vdst = v8t + bh * D * S_pad + ch * kChunk;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < D / 32; ++i) {
     const int idx = i * kThreads + tid;
     const int chn = idx >> 3, piece = idx & 7;
     const uint32_t* src = &tile[(chn * kVTileStride + piece * 16) / 4];
@@ -278,11 +299,31 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
   }
 }
 
+template <int D>
+hipError_t launch_prologue_d(const Bf16View& q, const Bf16View& k, const Bf16View& v, const PrologueShape& ps,
+                             int smooth_k, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t,
+                             float* v_scale, float* k_mean_out, const PrologueWs& ws, hipStream_t stream) {
+  const int64_t BH = ps.B * ps.H;
+  const int64_t nchunks = ps.S_pad / kChunk;
+  hipLaunchKernelGGL(stats_kernel<D>, dim3((unsigned)(BH * ps.nparts)), dim3(kThreads), 0, stream, q, k, v, ps.H,
+                     ps.S, ps.S_pad, ps.chunks_per_wg, ps.nparts, smooth_k, q8, q_scale, k8, k_scale, ws.ksum_part,
+                     ws.vmax_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(finalize_kernel<D>, dim3((unsigned)BH), dim3(D * kFinalizeSlices), 0, stream, ps.S, ps.nparts,
+                     smooth_k, ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, v_scale, k_mean_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_kernel<D>, dim3((unsigned)(BH * nchunks)), dim3(kThreads), 0, stream, k, v, ps.H, ps.S,
+                     ps.S_pad, smooth_k, ws.kmean, ws.vinv, k8, k_scale, v8t);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H) {
+PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H, int64_t D) {
   PrologueShape ps{};
-  ps.B = B; ps.S = S; ps.H = H;
+  ps.B = B; ps.S = S; ps.H = H; ps.D = D;
   ps.S_pad = padded_len(S);
   const int64_t nchunks = ps.S_pad / kChunk;
   const int64_t total = B * H * nchunks;
@@ -296,18 +337,18 @@ PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t prologue_ws_bytes(const PrologueShape& ps) {
-  const size_t bh = (size_t)(ps.B * ps.H);
-  return align256(bh * ps.nparts * kHeadDim * sizeof(double)) + align256(bh * ps.nparts * kHeadDim * sizeof(float)) +
-         2 * align256(bh * kHeadDim * sizeof(float));
+  const size_t bh = (size_t)(ps.B * ps.H), D = (size_t)ps.D;
+  return align256(bh * ps.nparts * D * sizeof(double)) + align256(bh * ps.nparts * D * sizeof(float)) +
+         2 * align256(bh * D * sizeof(float));
 }
 
 PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps) {
-  const size_t bh = (size_t)(ps.B * ps.H);
+  const size_t bh = (size_t)(ps.B * ps.H), D = (size_t)ps.D;
   char* p = static_cast<char*>(ws);
   PrologueWs w{};
-  w.ksum_part = reinterpret_cast<double*>(p); p += align256(bh * ps.nparts * kHeadDim * sizeof(double));
-  w.vmax_part = reinterpret_cast<float*>(p); p += align256(bh * ps.nparts * kHeadDim * sizeof(float));
-  w.kmean = reinterpret_cast<float*>(p); p += align256(bh * kHeadDim * sizeof(float));
+  w.ksum_part = reinterpret_cast<double*>(p); p += align256(bh * ps.nparts * D * sizeof(double));
+  w.vmax_part = reinterpret_cast<float*>(p); p += align256(bh * ps.nparts * D * sizeof(float));
+  w.kmean = reinterpret_cast<float*>(p); p += align256(bh * D * sizeof(float));
   w.vinv = reinterpret_cast<float*>(p);
   return w;
 }
@@ -315,20 +356,11 @@ PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps) {
 hipError_t launch_prologue(const Bf16View& q, const Bf16View& k, const Bf16View& v, const PrologueShape& ps,
                            int smooth_k, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t,
                            float* v_scale, float* k_mean_out, const PrologueWs& ws, hipStream_t stream) {
-  const int64_t BH = ps.B * ps.H;
-  const int64_t nchunks = ps.S_pad / kChunk;
-  hipLaunchKernelGGL(stats_kernel, dim3((unsigned)(BH * ps.nparts)), dim3(kThreads), 0, stream, q, k, v, ps.H, ps.S,
-                     ps.S_pad, ps.chunks_per_wg, ps.nparts, smooth_k, q8, q_scale, k8, k_scale, ws.ksum_part,
-                     ws.vmax_part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(kHeadDim * kFinalizeSlices), 0, stream, ps.S,
-                     ps.nparts, smooth_k, ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, v_scale, k_mean_out);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)(BH * nchunks)), dim3(kThreads), 0, stream, k, v, ps.H, ps.S,
-                     ps.S_pad, smooth_k, ws.kmean, ws.vinv, k8, k_scale, v8t);
-  return hipGetLastError();
+  if (ps.D == 64)
+    return launch_prologue_d<64>(q, k, v, ps, smooth_k, q8, q_scale, k8, k_scale, v8t, v_scale, k_mean_out, ws,
+                                 stream);
+  return launch_prologue_d<128>(q, k, v, ps, smooth_k, q8, q_scale, k8, k_scale, v8t, v_scale, k_mean_out, ws,
+                                stream);
 }
 
 }  // namespace sage

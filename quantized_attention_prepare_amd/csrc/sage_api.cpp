@@ -51,8 +51,8 @@ sage_status check_tensor_args(const sage_tensor* t, const char* name) {
 // Step 2 checks (what the kernels accept) of a BF16 tensor argument.
 sage_status check_tensor_contract(const sage_tensor* t, const char* name, const int64_t* ref_size) {
   if (t->dtype != SAGE_BF16) return fail(SAGE_ERR_UNSUPPORTED, "%s: dtype %d is not BF16", name, t->dtype);
-  if (t->size[3] != sage::kHeadDim)
-    return fail(SAGE_ERR_UNSUPPORTED, "%s: head dim %lld is not 128", name, (long long)t->size[3]);
+  if (!sage::supported_head_dim(t->size[3]))
+    return fail(SAGE_ERR_UNSUPPORTED, "%s: head dim %lld is not 64 or 128", name, (long long)t->size[3]);
   if (ref_size)
     for (int i = 0; i < 4; ++i)
       if (t->size[i] != ref_size[i])
@@ -113,13 +113,13 @@ struct FusedWs {
   void* prologue;
 };
 
-size_t fused_bytes(int64_t B, int64_t S, int64_t H, FusedWs* carve, void* base) {
+size_t fused_bytes(int64_t B, int64_t S, int64_t H, int64_t D, FusedWs* carve, void* base) {
   const int64_t S_pad = sage::padded_len(S);
   const size_t bh = (size_t)(B * H);
-  const size_t tens = align256(bh * (size_t)S_pad * sage::kHeadDim);
+  const size_t tens = align256(bh * (size_t)S_pad * (size_t)D);
   const size_t sc = align256(bh * (size_t)(S_pad / sage::kQBlock) * sizeof(float));
-  const size_t vs = align256(bh * sage::kHeadDim * sizeof(float));
-  sage::PrologueShape ps = sage::prologue_shape(B, S, H);
+  const size_t vs = align256(bh * (size_t)D * sizeof(float));
+  sage::PrologueShape ps = sage::prologue_shape(B, S, H, D);
   const size_t pro = sage::prologue_ws_bytes(ps);
   if (carve) {
     char* p = static_cast<char*>(base);
@@ -138,7 +138,7 @@ sage_status prepare_impl(const sage_tensor* q, const sage_tensor* k, const sage_
                          float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
                          void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
-  sage::PrologueShape ps = sage::prologue_shape(B, S, H);
+  sage::PrologueShape ps = sage::prologue_shape(B, S, H, q->size[3]);
   hipError_t e = sage::launch_prologue(view(q), view(k), view(v), ps, smooth_k ? 1 : 0, q8, q_scale, k8, k_scale, v8t,
                                        v_scale, k_mean, sage::prologue_ws_carve(ws, ps), stream);
   (void)ws_bytes;
@@ -155,16 +155,14 @@ int sage_kv_tile(void) { return sage::kKvTile; }
 int64_t sage_padded_len(int64_t S) { return sage::padded_len(S); }
 
 size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k) {
-  (void)D;
   (void)smooth_k;
-  if (B <= 0 || S <= 0 || H <= 0) return 0;
-  return sage::prologue_ws_bytes(sage::prologue_shape(B, S, H));
+  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D)) return 0;
+  return sage::prologue_ws_bytes(sage::prologue_shape(B, S, H, D));
 }
 
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
-  (void)D;
-  if (B <= 0 || S <= 0 || H <= 0) return 0;
-  return fused_bytes(B, S, H, nullptr, nullptr);
+  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D)) return 0;
+  return fused_bytes(B, S, H, D, nullptr, nullptr);
 }
 
 sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
@@ -204,7 +202,7 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
   if (want_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "null lse pointer");
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
-  if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld is not 128", (long long)D);
+  if (!sage::supported_head_dim(D)) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld is not 64 or 128", (long long)D);
   const int64_t want[4] = {B, S, H, D};
   if ((s = check_tensor_contract(o, "o", want))) return s;
   const void* ins[] = {q8, q_scale, k8, k_scale, v8t, v_scale};
@@ -214,7 +212,7 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
   if (empty) return ok();
   if ((s = check_device())) return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
-  hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, sm_scale, ov,
+  hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, ov,
                                         want_lse ? lse : nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -257,14 +255,14 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   if (empty) return ok();
   if ((s = check_device())) return s;
   FusedWs w{};
-  fused_bytes(B, S, H, &w, ws);
+  fused_bytes(B, S, H, q->size[3], &w, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = prepare_impl(q, k, v, smooth_k, w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, nullptr, w.prologue,
                         ws_bytes, st)))
     return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
-  hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, sm_scale, ov,
-                                        return_lse ? lse : nullptr, st);
+  hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, q->size[3],
+                                        sm_scale, ov, return_lse ? lse : nullptr, st);
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -5,7 +5,8 @@
 
 namespace sage {
 
-constexpr int kHeadDim = 128;   // D
+constexpr int kHeadDim = 128;   // the head dim of the pages' workloads; 64 is the other one built
+inline bool supported_head_dim(int64_t D) { return D == 64 || D == 128; }
 constexpr int kKvTile = 128;    // keys per online-softmax tile
 constexpr int kQBlock = 32;     // rows per INT8 quantization block
 constexpr int kChunk = 128;     // rows handled by one prologue workgroup pass
@@ -33,12 +34,12 @@ struct PrologueWs {
 };
 
 struct PrologueShape {
-  int64_t B, S, H, S_pad;
+  int64_t B, S, H, D, S_pad;
   int chunks_per_wg;   // 128-row chunks folded into one statistics workgroup
   int64_t nparts;      // statistics partials per head
 };
 
-PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H);
+PrologueShape prologue_shape(int64_t B, int64_t S, int64_t H, int64_t D);
 size_t prologue_ws_bytes(const PrologueShape& ps);
 PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps);
 
@@ -47,7 +48,7 @@ hipError_t launch_prologue(const Bf16View& q, const Bf16View& k, const Bf16View&
                            float* v_scale, float* k_mean_out, const PrologueWs& ws, hipStream_t stream);
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
-                            const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H,
+                            const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                             float sm_scale, const Bf16OutView& o, float* lse, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers

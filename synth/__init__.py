@@ -139,6 +139,12 @@ def _workloads():
     w["C5"] = Workload("C5", 5, 8, 28, 384, 128, False, _normal(5, 0),
                        TensorSpec(OUTLIERS, seed(5, 1), seed(5, 3), seed(5, 4), 0.01, 20.0), _normal(5, 2), None,
                        "many short calls B=8 H=28 S=384, 1% K outliers N(0,20^2)")
+    # head dim 64 (an extension beyond the pages' D = 128): the video-DiT-like
+    # token count with the same H * D as C3
+    w["C6"] = Workload("C6", 6, 1, 56, 32768, 64, True,
+                       TensorSpec(HEAD_SCALE, seed(6, 0), seed(6, 3), 0, 0.5, 3.0),
+                       TensorSpec(HEAD_SCALE, seed(6, 1), seed(6, 3) + 1_000_000, 0, 0.5, 3.0),
+                       _normal(6, 2), 8192, "head dim 64: B=1 H=56 S=32768 D=64, per-head scales U[0.5,3]")
     return w
 
 

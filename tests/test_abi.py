@@ -40,6 +40,10 @@ def test_constants_and_sizes():
     # the quantized tensors alone: 3 * B*H*S_pad*128 bytes
     assert big >= 3 * 28 * 32768 * 128
     assert L.sage_prepare_workspace_bytes(1, 4096, 28, 128, 1) > 0
+    # head dim 64: half the quantized bytes; other head dims are not supported (0 bytes)
+    assert 0 < L.sage_fused_workspace_bytes(1, 32768, 28, 64) < big
+    assert L.sage_fused_workspace_bytes(1, 32768, 28, 64) >= 3 * 28 * 32768 * 64
+    assert L.sage_fused_workspace_bytes(1, 256, 2, 96) == 0
     for s in range(5):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
 
@@ -101,8 +105,9 @@ def test_fused_validation_order_on_host():
     assert fused(h, causal=1) == UNSUPPORTED and "causal" in last_error()
     assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value + 2)) == UNSUPPORTED and "lse" in last_error()
     assert fused(h, q=h.tensor(dtype=2), k=h.tensor(dtype=2), v=h.tensor(dtype=2), o=h.tensor(dtype=2)) == UNSUPPORTED
-    d64 = (1, 64, 2, 64)
-    assert fused(h, q=h.tensor(d64), k=h.tensor(d64), v=h.tensor(d64), o=h.tensor(d64)) == UNSUPPORTED
+    d96 = (1, 64, 2, 96)
+    assert fused(h, q=h.tensor(d96), k=h.tensor(d96), v=h.tensor(d96), o=h.tensor(d96)) == UNSUPPORTED
+    assert "64 or 128" in last_error()
     assert fused(h, k=h.tensor((1, 65, 2, 128))) == UNSUPPORTED and "shape" in last_error()
     assert fused(h, v=h.tensor(stride=(64 * 256, 256, 128, 2))) == UNSUPPORTED
     assert fused(h, o=h.tensor(stride=(64 * 256, 260, 128, 1))) == UNSUPPORTED
@@ -114,6 +119,9 @@ def test_fused_validation_order_on_host():
     # 4. with everything valid, the device check is last: no GPU here
     rc = fused(h)
     assert rc == UNSUPPORTED and ("device" in last_error().lower())
+    d64 = (1, 64, 2, 64)   # the other head dim: valid up to the device check
+    assert fused(h, q=h.tensor(d64), k=h.tensor(d64), v=h.tensor(d64), o=h.tensor(d64)) == UNSUPPORTED
+    assert "device" in last_error().lower()
     assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value)) == UNSUPPORTED and "device" in last_error().lower()
 
 
@@ -147,7 +155,10 @@ def test_prepare_and_attn_validation_on_host():
     assert at(S=-1) == INVALID
     assert at(ptrs=[ctypes.c_void_p(0)] + ptrs[1:]) == INVALID
     assert at(sm=float("nan")) == INVALID
-    assert at(D=64) == UNSUPPORTED
+    assert at(D=96) == UNSUPPORTED and "64 or 128" in last_error()
+    assert at(D=64) == UNSUPPORTED          # o is (1, 64, 2, 128): shape mismatch
+    o64 = h.tensor((1, 64, 2, 64))
+    assert at(D=64, o=o64) == UNSUPPORTED and "device" in last_error().lower()
     assert at(S=65) == UNSUPPORTED          # o's shape differs from (B, S, H, D)
     assert at() == UNSUPPORTED and "device" in last_error().lower()
 

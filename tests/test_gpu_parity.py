@@ -222,6 +222,58 @@ def test_lse_workload_rows(sage, name):
     check_lse(f"lse_{name}", g, lse_o)
 
 
+# ------------------------------------------------------------------ head dim 64
+@pytest.mark.parametrize("B,S,H,smooth_k", [(1, 1, 1, False), (2, 33, 3, True), (1, 300, 2, False),
+                                             (2, 1000, 3, True), (3, 127, 1, True)])
+def test_d64_prologue_attention_and_lse(sage, B, S, H, smooth_k):
+    import torch
+    w = synth.custom(B, S, H, D=64, smooth_k=smooth_k, base_seed=4000 + S)
+    q, k, v = inputs(w)
+    g = gpu_prepare(sage, q, k, v, smooth_k)
+    o = oracle.prepare(q, k, v, smooth_k)
+    check_prologue(g, o, S, smooth_k=smooth_k)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    R, lse_o = oracle.attn(o, w.sm_scale, want_lse=True)
+    E = oracle.exact(q, k, v, w.sm_scale)
+    compare_attention(f"d64_{B}x{S}x{H}", out.view(torch.int16).cpu().numpy().view(np.uint16), R, E)
+    check_lse(f"d64_lse{B}x{S}x{H}", lse.cpu().numpy(), lse_o)
+
+
+def test_d64_equals_d128_with_zero_channels(sage):
+    """Appending 64 zero channels changes nothing the method computes on the first
+    64 (see the oracle's pin of the same identity): the two GPU paths agree bit
+    for bit, outputs and log-sum-exp."""
+    import torch
+    w = synth.custom(2, 700, 3, D=64, smooth_k=True, base_seed=4100)
+    q, k, v = (to_dev(a) for a in inputs(w))
+    pad = [torch.nn.functional.pad(x, (0, 64)) for x in (q, k, v)]
+    o64, l64 = sage.sageattn(q, k, v, sm_scale=0.125, return_lse=True)
+    o128, l128 = sage.sageattn(*pad, sm_scale=0.125, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o64.view(torch.int16), o128[..., :64].contiguous().view(torch.int16))
+    assert not o128[..., 64:].any()
+    assert torch.equal(l64.view(torch.int32), l128.view(torch.int32))
+
+
+def test_d64_workload_rows(sage):
+    import torch
+    w = synth.WORKLOADS["C6"]
+    q, k, v = inputs(w)
+    g = gpu_prepare(sage, q, k, v, w.smooth_k)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, True, w.smooth_k)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, 1024)
+    heads = sorted({(int(b), int(h)) for b, h, _ in rows})
+    prep = oracle.prepare(q, k, v, w.smooth_k, heads=heads)
+    check_prologue(g, prep, w.S, heads=heads[:6])
+    R, lse_o = oracle.attn(prep, w.sm_scale, rows=rows, want_lse=True)
+    E = oracle.exact(q, k, v, w.sm_scale, rows=rows)
+    O = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    compare_attention("C6", O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E)
+    check_lse("lse_C6", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
+
+
 def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     import torch
     w = synth.custom(2, 700, 3, smooth_k=True, base_seed=3000)
@@ -271,9 +323,9 @@ def test_unsupported_inputs_raise(sage):
         sage.sageattn(q, q, q, is_causal=True)
     with pytest.raises(NotImplementedError):
         sage.sageattn(q.half(), q.half(), q.half())
-    q64 = torch.zeros((1, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    q96 = torch.zeros((1, 64, 2, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
-        sage.sageattn(q64, q64, q64)
+        sage.sageattn(q96, q96, q96)
     k = torch.zeros((1, 65, 2, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
         sage.sageattn(q, k, k)
