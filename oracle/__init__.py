@@ -63,9 +63,10 @@ def lib():
         L.oracle_quant_block_int8.restype = ctypes.c_float
         L.oracle_prepare_head.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P, _P, _P]
         L.oracle_prepare_head.restype = ctypes.c_int
-        L.oracle_attn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, ctypes.c_float, _I, _P, _I, _P, _P, _P]
+        L.oracle_attn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, ctypes.c_float, _I, ctypes.c_int, _P, _I,
+                                       _P, _P, _P]
         L.oracle_attn_rows.restype = ctypes.c_int
-        L.oracle_exact_rows.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_double, _P, _I, _P, _P]
+        L.oracle_exact_rows.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_double, ctypes.c_int, _P, _I, _P, _P]
         L.oracle_exact_rows.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,12 +173,13 @@ def prepare(q: np.ndarray, k: np.ndarray, v: np.ndarray, smooth_k: bool, heads=N
 
 # ------------------------------------------------------------ attention
 def attn_rows_head(prep_head: dict, rows, sm_scale: float, T: int = KV_TILE, want_f32: bool = False,
-                   want_lse: bool = False):
+                   want_lse: bool = False, causal: bool = False):
     """Quantized attention for the given query rows of one head.
 
     prep_head holds that head's q8 [S,D], q_scale, k8, k_scale, v8t [D,S_pad],
     v_scale.  Returns BF16 bits [n, D], then (if asked) the pre-rounding float
     values and the rows' log-sum-exp of the dequantized scores (float [n]).
+    causal: row i sees keys 0 .. i only.
     """
     q8 = np.ascontiguousarray(prep_head["q8"])
     S, D = q8.shape
@@ -192,7 +194,8 @@ def attn_rows_head(prep_head: dict, rows, sm_scale: float, T: int = KV_TILE, wan
     k8 = np.ascontiguousarray(prep_head["k8"])
     lse = np.empty(n, np.float32) if want_lse else None
     rc = lib().oracle_attn_rows(_ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v8t), v8t.shape[1], _ptr(vs), S, D,
-                                float(sm_scale), int(T), _ptr(rows), n, _ptr(of), _ptr(ob), _ptr(lse))
+                                float(sm_scale), int(T), int(bool(causal)), _ptr(rows), n, _ptr(of), _ptr(ob),
+                                _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments")
     extra = ([of] if want_f32 else []) + ([lse] if want_lse else [])
@@ -204,7 +207,7 @@ def head_of(prep: dict, b: int, h: int) -> dict:
 
 
 def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None, chunk: int = 64,
-         want_lse: bool = False):
+         want_lse: bool = False, causal: bool = False):
     """Quantized attention over full-tensor prologue outputs.
 
     rows=None computes every row and returns BF16 bits [B, S, H, D] (and, with
@@ -220,7 +223,7 @@ def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None
         def job(j):
             b, h, s0 = j
             r = np.arange(s0, min(S, s0 + chunk), dtype=np.int64)
-            res = attn_rows_head(head_of(prep, b, h), r, sm_scale, T, want_lse=want_lse)
+            res = attn_rows_head(head_of(prep, b, h), r, sm_scale, T, want_lse=want_lse, causal=causal)
             if want_lse:
                 out[b, s0:s0 + r.size, h, :], lse_all[b, h, s0:s0 + r.size] = res
             else:
@@ -242,7 +245,7 @@ def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None
 
     def job2(j):
         b, h, idxs = j
-        res = attn_rows_head(head_of(prep, b, h), rows[idxs, 2], sm_scale, T, want_lse=want_lse)
+        res = attn_rows_head(head_of(prep, b, h), rows[idxs, 2], sm_scale, T, want_lse=want_lse, causal=causal)
         if want_lse:
             out[idxs], lse_rows[idxs] = res
         else:
@@ -253,23 +256,25 @@ def attn(prep: dict, sm_scale: float, rows=None, T: int = KV_TILE, nthreads=None
     return (out, lse_rows) if want_lse else out
 
 
-def exact_rows_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, sm_scale: float, want_lse: bool = False):
+def exact_rows_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, sm_scale: float, want_lse: bool = False,
+                    causal: bool = False):
     """fp64 exact attention rows of one head from dense [S, D] BF16 arrays
-    (and, if asked, each row's ln sum_j exp(q.k_j * sm_scale))."""
+    (and, if asked, each row's ln sum_j exp(q.k_j * sm_scale)); causal: keys j <= i."""
     q, k, v = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v))
     S, D = q.shape
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     out = np.empty((rows.size, D), np.float64)
     lse = np.empty(rows.size, np.float64) if want_lse else None
-    rc = lib().oracle_exact_rows(_ptr(q), _ptr(k), _ptr(v), S, D, D, float(sm_scale), _ptr(rows), rows.size,
-                                 _ptr(out), _ptr(lse))
+    rc = lib().oracle_exact_rows(_ptr(q), _ptr(k), _ptr(v), S, D, D, float(sm_scale), int(bool(causal)), _ptr(rows),
+                                 rows.size, _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_exact_rows rejected its arguments")
     return (out, lse) if want_lse else out
 
 
-def exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, rows=None, nthreads=None, chunk: int = 32):
-    """fp64 exact attention over [B, S, H, D] BF16 tensors (all rows, or (b,h,s) rows)."""
+def exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, rows=None, nthreads=None, chunk: int = 32,
+          causal: bool = False):
+    """fp64 exact attention over [B, S, H, D] BF16 tensors (all rows, or (b,h,s) rows); causal: keys j <= i."""
     B, S, H, D = q.shape
     L = lib()
     rs = H * D
@@ -279,8 +284,8 @@ def exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, rows=Non
         rr = np.ascontiguousarray(rr, dtype=np.int64)
         o = np.empty((rr.size, D), np.float64)
         rc = L.oracle_exact_rows(ctypes.c_void_p(q.ctypes.data + off), ctypes.c_void_p(k.ctypes.data + off),
-                                 ctypes.c_void_p(v.ctypes.data + off), S, D, rs, float(sm_scale), _ptr(rr), rr.size,
-                                 _ptr(o), None)
+                                 ctypes.c_void_p(v.ctypes.data + off), S, D, rs, float(sm_scale), int(bool(causal)),
+                                 _ptr(rr), rr.size, _ptr(o), None)
         if rc != 0:
             raise ValueError("oracle_exact_rows rejected its arguments")
         return o

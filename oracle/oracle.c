@@ -182,10 +182,13 @@ int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *     uses the whole FP8 range), PV accumulated in float as
  *     o_d = alpha*o_d + sum_tile dec(p8_j) * dec(v8[j,d]);
  *   - output bf16((o_d * v_scale[d]) / (448 * l)).
- * Sums inside a tile run in ascending key order. */
+ * Sums inside a tile run in ascending key order.
+ * Causal (an extension: the pages reject it): query i sees keys 0 .. i only,
+ * i.e. the row is computed exactly as above over the first i + 1 keys, with
+ * the same tiles from key 0 (the last one cut at key i). */
 int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                      const uint8_t* v8t, int64_t S_pad, const float* v_scale, int64_t S, int64_t D, float sm_scale,
-                     int64_t T, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16,
+                     int64_t T, int causal, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16,
                      float* lse_out) {
   if (S < 1 || D < 1 || T < 1 || S_pad < S) return -1;
   const float log2e = 1.44269504088896340736f;
@@ -203,8 +206,9 @@ int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, c
     float m = -INFINITY, l = 0.0f;
     for (int64_t d = 0; d < D; ++d) o[d] = 0.0f;
 
-    for (int64_t j0 = 0; j0 < S; j0 += T) {
-      int64_t n = (S - j0 < T) ? S - j0 : T;
+    const int64_t nk = causal ? i + 1 : S;   /* keys this row sees */
+    for (int64_t j0 = 0; j0 < nk; j0 += T) {
+      int64_t n = (nk - j0 < T) ? nk - j0 : T;
       float tmax = -INFINITY;
       for (int64_t jj = 0; jj < n; ++jj) {
         int64_t j = j0 + jj;
@@ -247,18 +251,19 @@ int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, c
 }
 
 /* Exact attention in double: softmax(q k^T * sm_scale) v, the quantity the
- * method approximates (no quantization, no tiling). */
+ * method approximates (no quantization, no tiling); causal: keys j <= i. */
 int oracle_exact_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S, int64_t D,
-                      int64_t row_stride, double sm_scale, const int64_t* rows, int64_t nrows, double* out,
-                      double* lse_out) {
+                      int64_t row_stride, double sm_scale, int causal, const int64_t* rows, int64_t nrows,
+                      double* out, double* lse_out) {
   if (S < 1 || D < 1) return -1;
   double* s = (double*)malloc((size_t)S * sizeof(double));
   if (!s) return -1;
   for (int64_t r = 0; r < nrows; ++r) {
     int64_t i = rows[r];
     if (i < 0 || i >= S) { free(s); return -1; }
+    const int64_t nk = causal ? i + 1 : S;   /* keys j <= i when causal */
     double mx = -INFINITY;
-    for (int64_t j = 0; j < S; ++j) {
+    for (int64_t j = 0; j < nk; ++j) {
       double acc = 0.0;
       for (int64_t d = 0; d < D; ++d)
         acc += (double)oracle_bf16_decode(q[i * row_stride + d]) * (double)oracle_bf16_decode(k[j * row_stride + d]);
@@ -266,11 +271,11 @@ int oracle_exact_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
       if (s[j] > mx) mx = s[j];
     }
     double den = 0.0;
-    for (int64_t j = 0; j < S; ++j) { s[j] = exp(s[j] - mx); den += s[j]; }
+    for (int64_t j = 0; j < nk; ++j) { s[j] = exp(s[j] - mx); den += s[j]; }
     if (lse_out) lse_out[r] = mx + log(den);   /* ln sum_j e^(s_j) */
     for (int64_t d = 0; d < D; ++d) {
       double num = 0.0;
-      for (int64_t j = 0; j < S; ++j) num += s[j] * (double)oracle_bf16_decode(v[j * row_stride + d]);
+      for (int64_t j = 0; j < nk; ++j) num += s[j] * (double)oracle_bf16_decode(v[j * row_stride + d]);
       out[r * D + d] = num / den;
     }
   }

@@ -70,18 +70,19 @@ int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * out_bf16[n][D] the BF16 result; lse_out[n] (may be NULL) the natural-log
  * sum of exponentials of the row's dequantized scores, m ln 2 + ln l from the
  * final running maximum m (log2 units) and l = sum_j 2^(t_j - m), evaluated
- * in double and rounded once to float. Returns 0, or -1 for bad arguments. */
+ * in double and rounded once to float. causal != 0: row i sees keys 0 .. i
+ * only (same tiles from key 0). Returns 0, or -1 for bad arguments. */
 int oracle_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                      const uint8_t* v8t, int64_t S_pad, const float* v_scale, int64_t S, int64_t D, float sm_scale,
-                     int64_t T, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16,
+                     int64_t T, int causal, const int64_t* rows, int64_t nrows, float* out_f32, uint16_t* out_bf16,
                      float* lse_out);
 
 /* Exact softmax(q k^T * sm_scale) v in double for selected rows of one head,
  * from the unquantized BF16 inputs (same addressing as oracle_prepare_head);
  * lse_out[n] (may be NULL) receives ln sum_j exp(q.k_j * sm_scale). */
 int oracle_exact_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S, int64_t D,
-                      int64_t row_stride, double sm_scale, const int64_t* rows, int64_t nrows, double* out,
-                      double* lse_out);
+                      int64_t row_stride, double sm_scale, int causal, const int64_t* rows, int64_t nrows,
+                      double* out, double* lse_out);
 
 #ifdef __cplusplus
 }
