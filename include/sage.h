@@ -10,9 +10,12 @@
  *     subtracted from K first;
  *   - the attention step computes QK^T in INT8 and PV in FP8, both with FP32
  *     accumulation, and writes BF16;
- *   - accepted inputs are BF16 [B, S, H, 128] with equal Q/K/V shapes, no
- *     mask, non-causal; anything else is rejected with an error, never
- *     silently handled another way.
+ *   - accepted inputs are BF16 [B, S, H, 128] with equal Q/K/V shapes and no
+ *     mask; anything else is rejected with an error, never silently handled
+ *     another way.
+ * Extensions beyond the pages (whose package rejects them): head dim 64
+ * (the layouts below then hold 64 where they say 128), the per-row
+ * log-sum-exp output, and causal attention (query i sees keys 0 .. i).
  *
  * Conventions for every call:
  *   - All calls are asynchronous on `stream` (a hipStream_t; NULL is the
@@ -23,7 +26,7 @@
  *   - Validation is done on the host before any device call, in this order:
  *       1. null pointers, negative sizes, non-finite or non-positive sm_scale
  *          -> SAGE_ERR_INVALID_ARGUMENT;
- *       2. causal, LSE, dtype other than BF16, D != 128, unequal shapes,
+ *       2. dtype other than BF16, D not 64 or 128, unequal shapes,
  *          stride[3] != 1, a base address / row stride that is not 16-byte
  *          aligned, or S > 2^25 (33,554,432 tokens) -> SAGE_ERR_UNSUPPORTED;
  *       3. workspace smaller than the *_workspace_bytes() figure
@@ -125,15 +128,26 @@ sage_status sage_attn_lse(const int8_t* q8, const float* q_scale, const int8_t* 
                           const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                           float sm_scale, const sage_tensor* o, float* lse, void* stream);
 
+/* sage_attn with both extensions selectable: is_causal != 0 masks key j for
+ * query i when j > i (the usual causal mask for equal query and key lengths;
+ * the key tiles still start at key 0, so row i is exactly the non-causal
+ * computation over keys 0 .. i), and a non-NULL lse receives the rows'
+ * log-sum-exp as in sage_attn_lse (over the keys the row sees). lse = NULL
+ * writes none. Same layouts, alignment and errors as sage_attn. */
+sage_status sage_attn_ex(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                         const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                         float sm_scale, int is_causal, const sage_tensor* o, float* lse, void* stream);
+
 /* Device workspace sage_attn_fused needs: the quantized tensors, their
  * scales and the prologue's statistics. */
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /* sage_prepare then sage_attn on one stream: the C image of
  * sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse) (issue,
- * "What I have so far"). is_causal must be 0 (causal attention is rejected, as
- * on the pages). return_lse = 1 also writes lse as sage_attn_lse does (lse
- * non-NULL); return_lse = 0 requires lse NULL (else SAGE_ERR_INVALID_ARGUMENT). */
+ * "What I have so far"). is_causal != 0 selects the causal mask of sage_attn_ex
+ * (an extension: the pages' package rejects it). return_lse = 1 also writes lse
+ * as sage_attn_lse does (lse non-NULL); return_lse = 0 requires lse NULL (else
+ * SAGE_ERR_INVALID_ARGUMENT). */
 sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
                             int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
                             size_t ws_bytes, void* stream);

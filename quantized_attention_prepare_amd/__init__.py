@@ -16,7 +16,8 @@ softmax_scale, ...)):
            return_lse=False, smooth_k=True)
   gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k=True)
   prepare(q, k, v, smooth_k)            -> dict of quantized tensors
-  attn(prepared, sm_scale, out=None, return_lse=False) -> BF16 output (, lse)
+  attn(prepared, sm_scale, out=None, return_lse=False, is_causal=False)
+                                        -> BF16 output (, lse)
 """
 from __future__ import annotations
 
@@ -85,6 +86,9 @@ def lib():
         L.sage_attn.restype = ctypes.c_int
         L.sage_attn_lse.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P, _P]
         L.sage_attn_lse.restype = ctypes.c_int
+        L.sage_attn_ex.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, ctypes.c_int, _T, _P,
+                                   _P]
+        L.sage_attn_ex.restype = ctypes.c_int
         L.sage_attn_fused.argtypes = [_T, _T, _T, _T, ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_int,
                                       _P, ctypes.c_size_t, _P]
         L.sage_attn_fused.restype = ctypes.c_int
@@ -171,9 +175,11 @@ def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None) ->
     return out
 
 
-def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = False, lse=None):
+def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = False, lse=None,
+         is_causal: bool = False):
     """Attention step on prepare()'s output; returns BF16 [B, S, H, D], and with
-    return_lse also the rows' log-sum-exp, float32 [B, H, S] (sage_attn_lse)."""
+    return_lse also the rows' log-sum-exp, float32 [B, H, S] (sage_attn_lse).
+    is_causal: query i sees keys 0 .. i (sage_attn_ex)."""
     import torch
     B, H, Sp, D = prep["q8"].shape
     S = prep["S"]
@@ -182,13 +188,15 @@ def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = 
     to = describe(out)
     args = (_ptr(prep["q8"]), _ptr(prep["q_scale"]), _ptr(prep["k8"]), _ptr(prep["k_scale"]), _ptr(prep["v8t"]),
             _ptr(prep["v_scale"]), B, S, H, D, float(sm_scale), ctypes.byref(to))
-    if not return_lse:
-        check(lib().sage_attn(*args, _stream(stream)))
-        return out
-    if lse is None:
+    if return_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=prep["q8"].device)
-    check(lib().sage_attn_lse(*args, _ptr(lse), _stream(stream)))
-    return out, lse
+    if is_causal:
+        check(lib().sage_attn_ex(*args[:11], 1, args[11], _ptr(lse) if return_lse else None, _stream(stream)))
+    elif not return_lse:
+        check(lib().sage_attn(*args, _stream(stream)))
+    else:
+        check(lib().sage_attn_lse(*args, _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
 
 
 def fused_workspace_bytes(B: int, S: int, H: int, D: int = HEAD_DIM) -> int:
@@ -201,9 +209,9 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
 
     q, k, v: BF16 [B, S, H, D] ("NHD") or [B, H, S, D] ("HND"), equal shapes, D = 128
     (the pages' head dim) or 64.
-    Causal attention is rejected (NotImplementedError). return_lse=True also
+    is_causal=True lets query i see keys 0 .. i only, and return_lse=True also
     returns the rows' log-sum-exp of the dequantized scores, float32 [B, H, S]
-    (an extension: the pages' sageattn rejects it).
+    (both extensions: the pages' sageattn rejects them).
     """
     import torch
     if sm_scale is None:

@@ -104,26 +104,29 @@ SAGE_INLINE uint8_t* opaque_lds(uint8_t* dst) {
   return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t)a;
 }
 template <int D>
-SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t,
-                        const uint32_t (&lane_off)[Dim<D>::kCopyInstr], int wave) {
+SAGE_INLINE void load_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rk, int t, const uint32_t* lane_off, int wave) {
   constexpr int C = Dim<D>::kCopyInstr;
   dst = opaque_lds(dst);
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass has no LDS-destination buffer load
 #pragma unroll
   for (int i = 0; i < C; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(dst + 1024 * (C * wave + i)), 16, lane_off[i],
                                              (uint32_t)t * Dim<D>::kTileBytes + 1024u * (C * wave + i), 0, 0);
+#endif
 }
 // V tile t: D channels x 128 keys; channel rows are S_pad bytes apart in v8t
 // (head extent D * S_pad B); each KB is 8 channel rows.
 template <int D>
-SAGE_INLINE void load_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rv, int t, uint32_t S_pad,
-                        const uint32_t (&lane_off)[Dim<D>::kCopyInstr], int wave) {
+SAGE_INLINE void load_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rv, int t, uint32_t S_pad, const uint32_t* lane_off,
+                        int wave) {
   constexpr int C = Dim<D>::kCopyInstr;
   dst = opaque_lds(dst);
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
   for (int i = 0; i < C; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(dst + 1024 * (C * wave + i)), 16, lane_off[i],
                                              (uint32_t)t * kKvTile + (uint32_t)(8 * (C * wave + i)) * S_pad, 0, 0);
+#endif
 }
 
 SAGE_INLINE uint32_t pack_bf16x2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
@@ -238,10 +241,16 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
 // made only of padding come with cblk = +inf (probability exactly 0), and in
 // the partly padded block the padded keys' probability, which only matters for
 // l (their V codes are 0), is subtracted from l afterwards.
+// In general a masked tile (masked = true) gives each lane its own limit lim:
+// the lane sees the tile's keys below lim. Causal attention's diagonal tile
+// uses lim = min(query + 1, nvalid) (tile-relative), with cblk = +inf for the
+// blocks no lane of the wave sees; each lane then has at most one partly
+// masked block, whose masked keys' probability comes off l as above. Their
+// FP8 codes, which meet real V codes there, are cleared before that tile's PV.
 template <int D, bool kHasPrev>
 SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4], const float (&cblk)[4],
-                                int nvalid, const uint8_t* vbuf_prev, const uint8_t* kbuf_next, const uint8_t* qrow,
-                                int half, int col, int prow) {
+                                bool masked, int lim, const uint8_t* vbuf_prev, const uint8_t* kbuf_next,
+                                const uint8_t* qrow, int half, int col, int prow) {
   const int kbase = 16 * half;
   const int fk = Dim<D>::fk(prow);   // K swizzle of rows 32 kb + prow
   const int fq = Dim<D>::fq(col);    // Q swizzle of row col
@@ -250,12 +259,12 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
   // ---- slot 0: first V operand; tail masking; max of blocks 0, 1
   v8i vop;
   if (kHasPrev) vop = v_operand(vbuf_prev, 0, 0, half, col, fv);
-  if (nvalid < kKvTile) {
+  if (masked) {
     // Only the last tile gets here. The empty asm hides that nvalid is then
     // the loop-invariant length of the last tile, which would otherwise move
     // the 64 key-index comparisons out of the loop into live lane masks; the
     // selection uses sign masks rather than comparisons for the same reason.
-    int nv = nvalid - kbase;
+    int nv = lim - kbase;
     asm volatile("" : "+v"(nv));
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -284,10 +293,11 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
 #define SAGE_L_UPDATE()                                                                               \
   {                                                                                                   \
     float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                   \
-    if (nvalid < kKvTile && (nvalid & 31)) {                                                          \
-      const int kbp = nvalid >> 5; /* the partly padded block */                                      \
-      const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - nvalid));                              \
-      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, cblk[kbp], -moff));   \
+    if (masked && (lim & 31)) {                                                                       \
+      const int kbp = lim >> 5; /* the partly masked block */                                         \
+      const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - lim));                                 \
+      const float ck = cblk[kbp];                                                                     \
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, ck, -moff));           \
       if (nmask > 0) psum -= (float)nmask * pm;                                                       \
     }                                                                                                 \
     st.l_run = alpha * st.l_run + psum;                                                               \
@@ -397,7 +407,7 @@ SAGE_INLINE void pv_tile(WaveState<D>& st, const uint8_t* vbuf, int half, int co
                                                                    st.oacc[d], 0, 0, 0, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool kCausal>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, const int8_t* __restrict__ k8,
             const float* __restrict__ k_scale, const uint8_t* __restrict__ v8t, const float* __restrict__ v_scale,
@@ -430,7 +440,12 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const int64_t bid = blockIdx.x;
   const int64_t per = nwg / 8, rem = nwg % 8, x = bid % 8;
   const int64_t logical = x * per + (x < rem ? x : rem) + bid / 8;
-  const int64_t bh = logical / nqt, qt = logical % nqt;
+  const int64_t bh = logical / nqt;
+  // Causal: query tile qt costs qt + 1 key tiles. Each head's tiles are taken
+  // longest, shortest, second longest, ... so that every contiguous range of
+  // the order (one XCD's share) holds a balanced mix, longest first.
+  int64_t qt = logical % nqt;
+  if (kCausal) qt = (qt & 1) ? qt >> 1 : nqt - 1 - (qt >> 1);
   const int64_t b = bh / H, h = bh % H;
 
   const int64_t q0 = qt * kQPerWg + 32 * wave;   // this wave's first query (one INT8 block)
@@ -482,10 +497,14 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 
   const int ntiles = (int)(S_pad / kKvTile);
   const int last_valid = (int)(S - (int64_t)(ntiles - 1) * kKvTile);   // valid keys in the last tile (1..128)
+  // key tiles this workgroup visits: causal stops at the tile of its own
+  // queries (a query tile is one key tile: 128 rows)
+  static_assert(kQPerWg == kKvTile, "causal tiling assumes query tile = key tile");
+  const int ntw = kCausal ? (int)qt + 1 : ntiles;
 
   // K(0), K(1) in; scores of tile 0.
   load_k<D>(KBUF(0), rk, 0, k_lane_off, wave);
-  if (ntiles > 1) load_k<D>(KBUF(1), rk, 1, k_lane_off, wave);
+  if (ntw > 1) load_k<D>(KBUF(1), rk, 1, k_lane_off, wave);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v16i sa[4], sb[4];   // scores of the current and the next tile; they swap roles every iteration
@@ -496,33 +515,54 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // entry K(t+1) and V(t-1) must be in LDS; K(t+2) goes to the buffer K(t)
   // occupied and V(t) to the one V(t-2) occupied. After the last tile the
   // score MFMAs read stale K bytes whose scores are never used.
+  // Causal: the last visited tile holds the workgroup's own queries; there
+  // the lane sees keys below min(32 wave + col + 1, nvalid), and blocks at or
+  // past min(32 (wave + 1), nvalid) are masked for the whole wave.
 #define SAGE_ITERATION(T_, HAS_PREV_, CUR_, NEXT_)                                                             \
   {                                                                                                            \
     const int t_ = (T_);                                                                                       \
     __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                      \
     __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                  \
-    if (t_ + 2 < ntiles) load_k<D>(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                \
+    if (t_ + 2 < ntw) load_k<D>(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                   \
     load_v<D>(VBUF(t_ & 1), rv, t_, spad32, v_lane_off, wave);                                                 \
     const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                                \
+    const bool diag = kCausal && t_ == ntw - 1;                                                                \
+    const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                             \
     const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                         \
-    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block made only of padding */        \
-    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nvalid ? INFINITY : (qs * kss[kb]) * sl2;             \
-    if (t_ + 1 < ntiles) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                            \
-    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, nvalid, VBUF((t_ + 1) & 1), KBUF((t_ + 1) & 1), qrow,  \
-                                 half, col, prow);                                                             \
+    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */   \
+    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;               \
+    if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                               \
+    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                              \
+                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((t_ + 1) & 1),         \
+                                 KBUF((t_ + 1) & 1), qrow, half, col, prow);                                   \
   }
   SAGE_ITERATION(0, false, sa, sb)
   int t = 1;
-  for (; t + 1 < ntiles; t += 2) {
+  for (; t + 1 < ntw; t += 2) {
     SAGE_ITERATION(t, true, sb, sa)
     SAGE_ITERATION(t + 1, true, sa, sb)
   }
-  if (t < ntiles) SAGE_ITERATION(t, true, sb, sa)
+  if (t < ntw) SAGE_ITERATION(t, true, sb, sa)
 #undef SAGE_ITERATION
+  if constexpr (kCausal) {
+    // Clear the FP8 codes of the diagonal tile's masked keys (those at or past
+    // lim), whose V codes are real: byte u of pk[kc][i] is key
+    // 32 kb + 16 half + 4 g + u of the tile, kb = 2 kc + i / 4, g = i % 4.
+    const int lim = min(32 * wave + col + 1, ntw == ntiles ? last_valid : kKvTile);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int base = 32 * (2 * kc + i / 4) + 16 * half + 4 * (i % 4);
+        const int nb = min(4, max(0, lim - base));   // valid bytes of the word
+        const uint32_t keep = nb == 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
+        st.pk[kc][i] &= (int)keep;
+      }
+  }
   // PV of the last tile
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  pv_tile<D>(st, VBUF((ntiles - 1) & 1), half, col);
+  pv_tile<D>(st, VBUF((ntw - 1) & 1), half, col);
 
   // ---- epilogue: O = o * v_scale / (448 l)
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
@@ -554,17 +594,22 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                             const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
-                            float sm_scale, const Bf16OutView& o, float* lse, hipStream_t stream) {
+                            float sm_scale, bool causal, const Bf16OutView& o, float* lse, hipStream_t stream) {
   const int64_t S_pad = padded_len(S);
   const int64_t nqt = (S_pad + kQPerWg - 1) / kQPerWg;
   const int64_t nwg = B * H * nqt;
   const float sl2 = sm_scale * kLog2e;
-  if (D == 64)
-    hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale,
-                       v8t, v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
-  else
-    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8, k_scale,
-                       v8t, v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse);
+#define SAGE_LAUNCH(D_, CAUSAL_)                                                                               \
+  hipLaunchKernelGGL((attn_kernel<D_, CAUSAL_>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, q8, q_scale, k8,   \
+                     k_scale, v8t, v_scale, H, S, S_pad, nqt, nwg, sl2, o, lse)
+  if (D == 64) {
+    if (causal) SAGE_LAUNCH(64, true);
+    else SAGE_LAUNCH(64, false);
+  } else {
+    if (causal) SAGE_LAUNCH(128, true);
+    else SAGE_LAUNCH(128, false);
+  }
+#undef SAGE_LAUNCH
   return hipGetLastError();
 }
 

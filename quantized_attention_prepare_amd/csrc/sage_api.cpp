@@ -1,9 +1,11 @@
 // C ABI of the quantized attention forward (declared in include/sage.h):
 // argument validation on the host, workspace carving, launches on the
 // caller's stream. Rejections follow the kernels-community issue
-// "aiter-sage-attention", "What I have so far": causal, LSE, non-BF16, head
-// dim other than 128, unequal Q/K/V shapes and the wrong GPU architecture
-// raise an error instead of falling back silently.
+// "aiter-sage-attention", "What I have so far": non-BF16 inputs, unequal
+// Q/K/V shapes and the wrong GPU architecture raise an error instead of
+// falling back silently; head dims other than 64 and 128 likewise. Causal
+// attention and the log-sum-exp output, which the issue's package rejects,
+// are offered here as extensions.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -192,7 +194,8 @@ sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_
 
 static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                              const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
-                             float sm_scale, const sage_tensor* o, float* lse, bool want_lse, void* stream) {
+                             float sm_scale, bool causal, const sage_tensor* o, float* lse, bool want_lse,
+                             void* stream) {
   sage_status s;
   if ((s = check_sizes(B, S, H, D))) return s;
   if ((s = check_tensor_args(o, "o"))) return s;
@@ -212,7 +215,7 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
   if (empty) return ok();
   if ((s = check_device())) return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
-  hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, ov,
+  hipError_t e = sage::launch_attention(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, causal, ov,
                                         want_lse ? lse : nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -221,13 +224,20 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
 sage_status sage_attn(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                       const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                       float sm_scale, const sage_tensor* o, void* stream) {
-  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, o, nullptr, false, stream);
+  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, false, o, nullptr, false, stream);
 }
 
 sage_status sage_attn_lse(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                           const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                           float sm_scale, const sage_tensor* o, float* lse, void* stream) {
-  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, o, lse, true, stream);
+  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, false, o, lse, true, stream);
+}
+
+sage_status sage_attn_ex(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                         const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
+                         float sm_scale, int is_causal, const sage_tensor* o, float* lse, void* stream) {
+  return attn_impl(q8, q_scale, k8, k_scale, v8t, v_scale, B, S, H, D, sm_scale, is_causal != 0, o, lse,
+                   lse != nullptr, stream);
 }
 
 sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
@@ -245,7 +255,6 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   if (!empty && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
   if (return_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "return_lse set but lse is null");
   if (!return_lse && lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "lse given but return_lse is 0");
-  if (is_causal) return fail(SAGE_ERR_UNSUPPORTED, "causal attention is not supported");
   if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
       (s = check_tensor_contract(v, "v", q->size)) || (s = check_tensor_contract(o, "o", q->size)))
     return s;
@@ -262,7 +271,7 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
     return s;
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
   hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, q->size[3],
-                                        sm_scale, ov, return_lse ? lse : nullptr, st);
+                                        sm_scale, is_causal != 0, ov, return_lse ? lse : nullptr, st);
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -49,7 +49,7 @@ hipError_t launch_prologue(const Bf16View& q, const Bf16View& k, const Bf16View&
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                             const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
-                            float sm_scale, const Bf16OutView& o, float* lse, hipStream_t stream);
+                            float sm_scale, bool causal, const Bf16OutView& o, float* lse, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

@@ -102,7 +102,6 @@ def test_fused_validation_order_on_host():
     # invalid beats unsupported
     assert fused(h, causal=1, sm=float("inf")) == INVALID
     # 2. unsupported contract
-    assert fused(h, causal=1) == UNSUPPORTED and "causal" in last_error()
     assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value + 2)) == UNSUPPORTED and "lse" in last_error()
     assert fused(h, q=h.tensor(dtype=2), k=h.tensor(dtype=2), v=h.tensor(dtype=2), o=h.tensor(dtype=2)) == UNSUPPORTED
     d96 = (1, 64, 2, 96)
@@ -115,7 +114,8 @@ def test_fused_validation_order_on_host():
     # 3. workspace
     assert fused(h, ws_bytes=10) == WS_SMALL
     # unsupported beats a small workspace
-    assert fused(h, causal=1, ws_bytes=10) == UNSUPPORTED
+    assert fused(h, q=h.tensor(dtype=2), k=h.tensor(dtype=2), v=h.tensor(dtype=2), o=h.tensor(dtype=2),
+                 ws_bytes=10) == UNSUPPORTED
     # 4. with everything valid, the device check is last: no GPU here
     rc = fused(h)
     assert rc == UNSUPPORTED and ("device" in last_error().lower())
@@ -123,6 +123,9 @@ def test_fused_validation_order_on_host():
     assert fused(h, q=h.tensor(d64), k=h.tensor(d64), v=h.tensor(d64), o=h.tensor(d64)) == UNSUPPORTED
     assert "device" in last_error().lower()
     assert fused(h, lse_flag=1, lse=ctypes.c_void_p(h.buf().value)) == UNSUPPORTED and "device" in last_error().lower()
+    # causal (an extension) is valid up to the device check as well
+    assert fused(h, causal=1) == UNSUPPORTED and "device" in last_error().lower()
+    assert fused(h, causal=1, ws_bytes=10) == WS_SMALL
 
 
 def test_empty_problem_returns_ok_without_device():
@@ -172,6 +175,18 @@ def test_prepare_and_attn_validation_on_host():
     z = (1, 0, 2, 128)
     oz = h.tensor(z)
     assert L.sage_attn_lse(*ptrs, 1, 0, 2, 128, 0.1, ctypes.byref(oz), None, None) == OK   # empty: nothing to write
+
+    def at_ex(causal, lse, S=64, D=128, sm=0.1, o=o):
+        return L.sage_attn_ex(*ptrs, 1, S, 2, D, sm, causal, ctypes.byref(o), lse, None)
+
+    # lse is optional here; causal and non-causal both reach the device check
+    for causal in (0, 1):
+        assert at_ex(causal, None) == UNSUPPORTED and "device" in last_error().lower()
+        assert at_ex(causal, h.buf()) == UNSUPPORTED and "device" in last_error().lower()
+        assert at_ex(causal, None, sm=0.0) == INVALID
+        assert at_ex(causal, ctypes.c_void_p(h.buf().value + 2)) == UNSUPPORTED and "aligned" in last_error()
+        assert at_ex(causal, None, D=96) == UNSUPPORTED and "64 or 128" in last_error()
+    assert L.sage_attn_ex(*ptrs, 1, 0, 2, 128, 0.1, 1, ctypes.byref(oz), None, None) == OK
 
 
 def test_python_binding_raises_typed_errors():

@@ -274,6 +274,65 @@ def test_d64_workload_rows(sage):
     check_lse("lse_C6", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
 
 
+# ------------------------------------------------------------------ causal
+@pytest.mark.parametrize("B,S,H,D,smooth_k", [(1, 1, 1, 128, False), (2, 33, 3, 128, True), (1, 128, 2, 128, False),
+                                               (1, 257, 2, 128, True), (2, 300, 3, 128, False),
+                                               (1, 700, 2, 128, True), (1, 1000, 2, 64, True),
+                                               (3, 127, 1, 64, False)])
+def test_causal_attention_and_lse(sage, B, S, H, D, smooth_k):
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=6000 + S + D)
+    q, k, v = inputs(w)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", True, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    R, lse_o = oracle.attn(oracle.prepare(q, k, v, smooth_k), w.sm_scale, want_lse=True, causal=True)
+    E = oracle.exact(q, k, v, w.sm_scale, causal=True)
+    compare_attention(f"causal{B}x{S}x{H}x{D}", out.view(torch.int16).cpu().numpy().view(np.uint16), R, E)
+    check_lse(f"causal_lse{B}x{S}x{H}x{D}", lse.cpu().numpy(), lse_o)
+
+
+def test_causal_last_row_is_the_non_causal_row(sage):
+    """The last query sees every key, and on the diagonal tile the cleared
+    codes of the padded keys multiplied V codes that are zero anyway: the
+    causal and non-causal kernels agree on that row bit for bit (output and
+    log-sum-exp). Through sage_attn_ex on prepare()'s output, the causal step
+    is also the fused call's causal result."""
+    import torch
+    w = synth.custom(2, 1000, 3, smooth_k=True, base_seed=6100)
+    q, k, v = (to_dev(a) for a in inputs(w))
+    prep = sage.prepare(q, k, v, True)
+    oc, lc = sage.attn(prep, w.sm_scale, return_lse=True, is_causal=True)
+    on, ln = sage.attn(prep, w.sm_scale, return_lse=True)
+    of = sage.sageattn(q, k, v, is_causal=True, sm_scale=w.sm_scale)
+    oc2 = sage.attn(prep, w.sm_scale, is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(oc[:, -1].view(torch.int16), on[:, -1].view(torch.int16))
+    assert torch.equal(lc[:, :, -1].view(torch.int32), ln[:, :, -1].view(torch.int32))
+    assert not torch.equal(oc[:, :-1].view(torch.int16), on[:, :-1].view(torch.int16))
+    assert torch.equal(of.view(torch.int16), oc.view(torch.int16))
+    assert torch.equal(oc2.view(torch.int16), oc.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,n", [("C2", 2048), ("C3", 768)])
+def test_causal_workload_rows(sage, name, n):
+    import torch
+    w = synth.WORKLOADS[name]
+    q, k, v = inputs(w)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", True, w.sm_scale, True, w.smooth_k)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, n)
+    # plus the rows on either side of two key-tile boundaries and the first and last row of head 0
+    extra = np.array([[0, 0, s] for s in (0, 1, 127, 128, 129, 255, 256, w.S - 1)], dtype=np.int64)
+    rows = np.unique(np.concatenate([rows, extra]), axis=0)
+    heads = sorted({(int(b), int(h)) for b, h, _ in rows})
+    prep = oracle.prepare(q, k, v, w.smooth_k, heads=heads)
+    R, lse_o = oracle.attn(prep, w.sm_scale, rows=rows, want_lse=True, causal=True)
+    E = oracle.exact(q, k, v, w.sm_scale, rows=rows, causal=True)
+    O = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    compare_attention(f"causal_{name}", O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E)
+    check_lse(f"causal_lse_{name}", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
+
+
 def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     import torch
     w = synth.custom(2, 700, 3, smooth_k=True, base_seed=3000)
@@ -319,8 +378,6 @@ def test_empty_problem_is_a_no_op(sage):
 def test_unsupported_inputs_raise(sage):
     import torch
     q = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(NotImplementedError):
-        sage.sageattn(q, q, q, is_causal=True)
     with pytest.raises(NotImplementedError):
         sage.sageattn(q.half(), q.half(), q.half())
     q96 = torch.zeros((1, 64, 2, 96), dtype=torch.bfloat16, device="cuda")
