@@ -28,8 +28,10 @@ MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense INT8 (POP/s) and FP8 (PFLOP/s): 5.0 P
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E: 8 TB/s
 
 
-def attn_flops(w) -> float:
-    return 4.0 * w.B * w.H * w.S * w.S * w.D
+def attn_flops(w, causal: bool = False) -> float:
+    """4*D ops per query-key pair the rows see: S^2 pairs per head, S(S+1)/2 when causal."""
+    pairs = w.S * (w.S + 1) / 2 if causal else float(w.S) * w.S
+    return 4.0 * w.B * w.H * pairs * w.D
 
 
 def prologue_compulsory_bytes(w) -> int:
@@ -77,7 +79,7 @@ def time_events(fn, iters: int, stream) -> float:
     return start.elapsed_time(end) / iters
 
 
-def measure(w, steps: int, warmup: int):
+def measure(w, steps: int, warmup: int, causal: bool = False):
     import torch
     import quantized_attention_prepare_amd as sage
     import synth
@@ -88,7 +90,7 @@ def measure(w, steps: int, warmup: int):
     ws = torch.empty(sage.fused_workspace_bytes(w.B, w.S, w.H, w.D), dtype=torch.uint8, device=q.device)
 
     def step():
-        sage.sageattn(q, k, v, "NHD", False, w.sm_scale, False, w.smooth_k, out=out, workspace=ws, stream=stream)
+        sage.sageattn(q, k, v, "NHD", causal, w.sm_scale, False, w.smooth_k, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -102,8 +104,8 @@ def measure(w, steps: int, warmup: int):
     prep = sage.prepare(q, k, v, w.smooth_k, stream=stream)
     o2 = torch.empty_like(q)
     for _ in range(max(1, warmup)):
-        sage.attn(prep, w.sm_scale, out=o2, stream=stream)
-    attn_ms = time_events(lambda: sage.attn(prep, w.sm_scale, out=o2, stream=stream), steps, stream)
+        sage.attn(prep, w.sm_scale, out=o2, stream=stream, is_causal=causal)
+    attn_ms = time_events(lambda: sage.attn(prep, w.sm_scale, out=o2, stream=stream, is_causal=causal), steps, stream)
     prep_ms = time_events(lambda: sage.prepare(q, k, v, w.smooth_k, stream=stream), steps, stream)
     torch.cuda.synchronize()
     del q, k, v, out, ws, prep, o2
@@ -150,7 +152,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C3")
-    ap.add_argument("--others", default="C1,C2,C4,C5,C6", help="comma list of further workloads to report ('' for none)")
+    ap.add_argument("--others", default="C1,C2,C4,C5,C6,C3:causal",
+                    help="comma list of further workloads to report, NAME or NAME:causal ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 512 MiB five times (reference for HBM byte counters)")
@@ -188,12 +191,15 @@ def main():
     pro_bytes = prologue_compulsory_bytes(w)
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
-        wo = synth.WORKLOADS[name]
-        ro = measure(wo, max(5, args.steps // 2), max(2, args.warmup // 2))
+        base, _, mode = name.partition(":")
+        causal = mode == "causal"
+        wo = synth.WORKLOADS[base]
+        ro = measure(wo, max(5, args.steps // 2), max(2, args.warmup // 2), causal=causal)
+        fo = attn_flops(wo, causal)
         others[name] = {"step_ms": round(ro["step_ms"], 4),
-                        "step_tflops": round(attn_flops(wo) / (ro["step_ms"] * 1e-3) / 1e12, 1),
+                        "step_tflops": round(fo / (ro["step_ms"] * 1e-3) / 1e12, 1),
                         "attn_ms": round(ro["attn_ms"], 4),
-                        "attn_tflops": round(attn_flops(wo) / (ro["attn_ms"] * 1e-3) / 1e12, 1),
+                        "attn_tflops": round(fo / (ro["attn_ms"] * 1e-3) / 1e12, 1),
                         "prologue_ms": round(ro["prologue_ms"], 4),
                         "prologue_gbs": round(prologue_compulsory_bytes(wo) / (ro["prologue_ms"] * 1e-3) / 1e9, 1)}
     line = {
