@@ -9,6 +9,7 @@ per-block INT8 K quantization on those inputs), the GPU must not fall more
 than 2e-4 below the oracle's own cosine.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -331,6 +332,77 @@ def test_causal_workload_rows(sage, name, n):
     O = out.view(torch.int16).cpu().numpy().view(np.uint16)
     compare_attention(f"causal_{name}", O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E)
     check_lse(f"causal_lse_{name}", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
+
+
+# ------------------------------------------------------------------ 64-bit offsets, graph capture
+def test_tensors_past_2_31_elements(sage):
+    """B*S*H*D = 3*65536*96*128 > 2^31 elements (4.8 GB per BF16 tensor): the
+    prologue's codes of the first, a middle and the last head are bit-exact and
+    the last head's attention rows (element offsets past 2^31) match the oracle.
+    Inputs are seeded normal draws made on the device."""
+    import torch
+    B, S, H, D = 3, 65536, 96, 128
+    assert B * S * H * D > 2 ** 31
+    gen = torch.Generator(device="cuda").manual_seed(7000)
+    q = torch.randn((B, S, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((B, S, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k.add_(0.5)
+    v = torch.randn((B, S, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    sm = 1.0 / math.sqrt(D)
+    prep = sage.prepare(q, k, v, True)
+    out = sage.attn(prep, sm)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 127, 128, 40000, S - 129, S - 2, S - 1], dtype=np.int64)
+    for b, h in ((0, 0), (1, 47), (B - 1, H - 1)):
+        host = [x[b, :, h, :].contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for x in (q, k, v)]
+        o = oracle.prepare_head(*host, True)
+        g = {key: prep[key][b, h].cpu().numpy() for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale",
+                                                            "k_mean")}
+        check_prologue({key: val[None, None] for key, val in g.items()},
+                       {key: val[None, None] for key, val in o.items()}, S)
+        if (b, h) == (B - 1, H - 1):
+            R = oracle.attn_rows_head(o, rows, sm)
+            E = oracle.exact_rows_head(*host, rows, sm)
+            G = out[b, :, h, :].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+            compare_attention("past_2^31_last_head", G, R, E)
+    del q, k, v, prep, out
+    torch.cuda.empty_cache()
+
+
+def test_fused_calls_replay_from_a_hip_graph(sage):
+    """sageattn, causal and not, captured in one HIP graph (the library launches
+    kernels only: no allocation, memset or synchronisation inside) and replayed
+    three times with eager work in between: every replay equals the eager result
+    bit for bit."""
+    import torch
+    w = synth.custom(2, 700, 3, smooth_k=True, base_seed=6200)
+    q, k, v = (to_dev(a) for a in inputs(w))
+    ref = [sage.sageattn(q, k, v, is_causal=c, sm_scale=w.sm_scale, return_lse=True) for c in (False, True)]
+    torch.cuda.synchronize()
+    nws = sage.fused_workspace_bytes(2, 700, 3, 128)
+    ws = [torch.empty(nws, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty_like(q) for _ in range(2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm up on the capture stream
+        for c in (False, True):
+            sage.sageattn(q, k, v, is_causal=c, sm_scale=w.sm_scale, out=outs[c], workspace=ws[c])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        lses = [sage.sageattn(q, k, v, is_causal=c, sm_scale=w.sm_scale, return_lse=True, out=outs[c],
+                              workspace=ws[c])[1] for c in (False, True)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outs + lses:
+            t.zero_()
+        ws[0].fill_(0xAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for c in (0, 1):
+            assert torch.equal(outs[c].view(torch.int16), ref[c][0].view(torch.int16)), c
+            assert torch.equal(lses[c].view(torch.int32), ref[c][1].view(torch.int32)), c
 
 
 def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
