@@ -440,12 +440,19 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   const int64_t bid = blockIdx.x;
   const int64_t per = nwg / 8, rem = nwg % 8, x = bid % 8;
   const int64_t logical = x * per + (x < rem ? x : rem) + bid / 8;
-  const int64_t bh = logical / nqt;
-  // Causal: query tile qt costs qt + 1 key tiles. Each head's tiles are taken
-  // longest, shortest, second longest, ... so that every contiguous range of
-  // the order (one XCD's share) holds a balanced mix, longest first.
+  int64_t bh = logical / nqt;
   int64_t qt = logical % nqt;
-  if (kCausal) qt = (qt & 1) ? qt >> 1 : nqt - 1 - (qt >> 1);
+  if (kCausal) {
+    // Causal: query tile qt costs qt + 1 key tiles. Workgroups go out longest
+    // first (every head's last query tile, then the one before, ...), so the
+    // short tiles fill in at the end, and each XCD receives every eighth of
+    // them, a balanced share. Consecutive query tiles of one head are B*H
+    // workgroups apart: with B*H = 4 (mod 8), as for 28 heads, a head's tiles
+    // alternate between two XCDs.
+    const int64_t nbh = nwg / nqt;
+    qt = nqt - 1 - bid / nbh;
+    bh = bid % nbh;
+  }
   const int64_t b = bh / H, h = bh % H;
 
   const int64_t q0 = qt * kQPerWg + 32 * wave;   // this wave's first query (one INT8 block)
