@@ -15,7 +15,7 @@ softmax_scale, ...)):
   sageattn(q, k, v, tensor_layout="NHD", is_causal=False, sm_scale=None,
            return_lse=False, smooth_k=True)
   gfx950_sage_attention(query, key, value, softmax_scale=None, smooth_k=True)
-  prepare(q, k, v, smooth_k)            -> dict of quantized tensors
+  prepare(q, k, v, smooth_k, reuse=None) -> dict of quantized tensors
   attn(prepared, sm_scale, out=None, return_lse=False, is_causal=False)
                                         -> BF16 output (, lse)
 """
@@ -150,23 +150,33 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None) -> dict:
-    """Run the prologue; returns the quantized tensors in the library's layouts."""
+def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None, reuse: dict | None = None) -> dict:
+    """Run the prologue; returns the quantized tensors in the library's layouts.
+
+    reuse: the dict a previous prepare() returned for the same B, S, H, D; its
+    tensors and workspace are written again instead of allocating new ones.
+    """
     import torch
     tq, tk, tv = describe(q, layout), describe(k, layout), describe(v, layout)
     B, S, H, D = tq.size
     Sp = padded_len(S)
     dev = q.device
-    out = dict(q8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-               q_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-               k8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-               k_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-               v8t=torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
-               v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev),
-               k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev))
     L = lib()
     nws = L.sage_prepare_workspace_bytes(B, S, H, D, int(bool(smooth_k)))
-    ws = torch.empty(max(int(nws), 1), dtype=torch.uint8, device=dev)
+    if reuse is not None:
+        if reuse["q8"].shape != (B, H, Sp, D) or reuse["S"] != S or reuse["_ws"].numel() < max(int(nws), 1):
+            raise ValueError("prepare(reuse=...) needs the result of a call with the same B, S, H, D")
+        out = reuse
+        ws = reuse["_ws"]
+    else:
+        out = dict(q8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+                   q_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+                   k8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+                   k_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+                   v8t=torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
+                   v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev),
+                   k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev))
+        ws = torch.empty(max(int(nws), 1), dtype=torch.uint8, device=dev)
     check(L.sage_prepare(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), int(bool(smooth_k)), _ptr(out["q8"]),
                          _ptr(out["q_scale"]), _ptr(out["k8"]), _ptr(out["k_scale"]), _ptr(out["v8t"]),
                          _ptr(out["v_scale"]), _ptr(out["k_mean"]), _ptr(ws), nws, _stream(stream)))

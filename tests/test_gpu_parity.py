@@ -423,6 +423,28 @@ def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     assert torch.equal(l3.view(torch.int32), l2.view(torch.int32))
 
 
+def test_prepare_reuse_rewrites_the_same_buffers(sage):
+    """prepare(reuse=...) writes a previous result's tensors again: same
+    storage, same bits as a fresh call, on other inputs of the same shape;
+    another shape is refused before any launch."""
+    import torch
+    w1 = synth.custom(2, 300, 3, smooth_k=True, base_seed=6300)
+    w2 = synth.custom(2, 300, 3, smooth_k=True, base_seed=6301)
+    a = [to_dev(x) for x in inputs(w1)]
+    b = [to_dev(x) for x in inputs(w2)]
+    p = sage.prepare(*a, True)
+    ptrs = {key: val.data_ptr() for key, val in p.items() if torch.is_tensor(val)}
+    p2 = sage.prepare(*b, True, reuse=p)
+    fresh = sage.prepare(*b, True)
+    torch.cuda.synchronize()
+    assert p2 is p and all(p[key].data_ptr() == ptr for key, ptr in ptrs.items())
+    for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale", "k_mean"):
+        assert torch.equal(p2[key], fresh[key]), key
+    c = [to_dev(x) for x in inputs(synth.custom(2, 400, 3, smooth_k=True, base_seed=6302))]
+    with pytest.raises(ValueError):
+        sage.prepare(*c, True, reuse=p)
+
+
 def test_hnd_layout_and_strided_output_match_nhd(sage):
     import torch
     w = synth.custom(2, 200, 3, smooth_k=True, base_seed=3100)
