@@ -220,6 +220,11 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
   // a move per word)
   int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
   dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
+  // keep the packing in its slot: left free, the compiler sinks the packs of
+  // one of the two unrolled tiles past the rescale branch into the loop
+  // latch, which keeps that tile's 64 float probabilities live across the
+  // branch (about 40 more VGPRs)
+  asm volatile("" ::"v"(dw));
   pk[kb >> 1][j >> 2] = dw;
 }
 
