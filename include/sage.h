@@ -24,11 +24,14 @@
  *   - The caller owns every buffer. The library never allocates, frees or
  *     synchronises, and keeps no state between calls.
  *   - Validation is done on the host before any device call, in this order:
- *       1. null pointers, negative sizes, non-finite or non-positive sm_scale
+ *       1. null pointers, negative sizes, a tensor whose element count
+ *          overflows 64 bits, non-finite or non-positive sm_scale
  *          -> SAGE_ERR_INVALID_ARGUMENT;
  *       2. dtype other than BF16, D not 64 or 128, unequal shapes,
  *          stride[3] != 1, a base address / row stride that is not 16-byte
- *          aligned, or S > 2^25 (33,554,432 tokens) -> SAGE_ERR_UNSUPPORTED;
+ *          aligned, strides reaching past 2^60 elements, S > 2^25
+ *          (33,554,432 tokens), or B * H * ceil(S / 128) >= 2^31 (the
+ *          workgroup count of a launch) -> SAGE_ERR_UNSUPPORTED;
  *       3. workspace smaller than the *_workspace_bytes() figure
  *          -> SAGE_ERR_WORKSPACE_TOO_SMALL;
  *       4. current device is not gfx950 (or there is none) -> SAGE_ERR_UNSUPPORTED;
@@ -86,7 +89,9 @@ int sage_kv_tile(void);
 /* S rounded up to a multiple of sage_kv_tile(); 0 for S <= 0. */
 int64_t sage_padded_len(int64_t S);
 
-/* Device workspace sage_prepare needs (per-chunk channel statistics). */
+/* Device workspace sage_prepare needs (per-chunk channel statistics); 0 for
+ * an empty or unsupported problem (non-positive size, D not 64 or 128, or a
+ * problem past the limits of validation step 2). */
 size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k);
 
 /* The prologue (issue, "The kernel"; release notes, "What changed"):
@@ -139,7 +144,8 @@ sage_status sage_attn_ex(const int8_t* q8, const float* q_scale, const int8_t* k
                          float sm_scale, int is_causal, const sage_tensor* o, float* lse, void* stream);
 
 /* Device workspace sage_attn_fused needs: the quantized tensors, their
- * scales and the prologue's statistics. */
+ * scales and the prologue's statistics; 0 when sage_prepare_workspace_bytes
+ * would be 0. */
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /* sage_prepare then sage_attn on one stream: the C image of

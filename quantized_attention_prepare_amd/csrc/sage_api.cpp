@@ -40,13 +40,36 @@ sage_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b for non-negative operands; false when the product overflows int64.
+bool mul_nonneg(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+// Whether the kernels can take B heads x H x S rows: every launch has at most
+// B * H * S_pad / 128 workgroups, which must fit a 32-bit grid. Sizes >= 0.
+bool extent_ok(int64_t B, int64_t S, int64_t H) {
+  if (S > sage::kMaxSeq) return false;
+  int64_t bh, tiles;
+  return mul_nonneg(B, H, &bh) && mul_nonneg(bh, sage::padded_len(S) / sage::kKvTile, &tiles) &&
+         tiles <= sage::kMaxTiles;
+}
+
+sage_status check_extent(int64_t B, int64_t S, int64_t H) {
+  if (!extent_ok(B, S, H))
+    return fail(SAGE_ERR_UNSUPPORTED, "problem too large: B=%lld S=%lld H=%lld (S <= 2^25 and B*H*ceil(S/128) < 2^31)",
+                (long long)B, (long long)S, (long long)H);
+  return SAGE_OK;
+}
+
 // Step 1 checks (pointer, sizes) of a BF16 tensor argument.
 sage_status check_tensor_args(const sage_tensor* t, const char* name) {
   if (!t) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: null tensor descriptor", name);
   for (int i = 0; i < 4; ++i)
     if (t->size[i] < 0) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: negative size[%d]", name, i);
-  const int64_t n = t->size[0] * t->size[1] * t->size[2] * t->size[3];
-  if (n > 0 && !t->data) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: null data pointer", name);
+  const bool empty = t->size[0] == 0 || t->size[1] == 0 || t->size[2] == 0 || t->size[3] == 0;
+  int64_t n = 1;
+  for (int i = 0; i < 4 && !empty; ++i)
+    if (!mul_nonneg(n, t->size[i], &n))
+      return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: element count overflows 64 bits", name);
+  if (!empty && !t->data) return fail(SAGE_ERR_INVALID_ARGUMENT, "%s: null data pointer", name);
   return SAGE_OK;
 }
 
@@ -67,6 +90,17 @@ sage_status check_tensor_contract(const sage_tensor* t, const char* name, const 
     if (t->stride[i] < 0 || (t->stride[i] % 8) != 0)
       return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[%d]=%lld is not a non-negative multiple of 8 elements", name, i,
                   (long long)t->stride[i]);
+  // the last element's offset (in elements) must fit, with room, in the
+  // kernels' 64-bit address arithmetic
+  if (t->size[0] > 0 && t->size[1] > 0 && t->size[2] > 0 && t->size[3] > 0) {
+    int64_t end = t->size[3];
+    for (int i = 0; i < 3; ++i) {
+      int64_t part;
+      if (!mul_nonneg(t->size[i] - 1, t->stride[i], &part) || __builtin_add_overflow(end, part, &end) ||
+          end > (int64_t(1) << 60))
+        return fail(SAGE_ERR_UNSUPPORTED, "%s: strides reach past 2^60 elements", name);
+    }
+  }
   if (!aligned16(t->data)) return fail(SAGE_ERR_UNSUPPORTED, "%s: data pointer not 16-byte aligned", name);
   return SAGE_OK;
 }
@@ -158,12 +192,12 @@ int64_t sage_padded_len(int64_t S) { return sage::padded_len(S); }
 
 size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k) {
   (void)smooth_k;
-  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D)) return 0;
+  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D) || !extent_ok(B, S, H)) return 0;
   return sage::prologue_ws_bytes(sage::prologue_shape(B, S, H, D));
 }
 
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
-  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D)) return 0;
+  if (B <= 0 || S <= 0 || H <= 0 || !sage::supported_head_dim(D) || !extent_ok(B, S, H)) return 0;
   return fused_bytes(B, S, H, D, nullptr, nullptr);
 }
 
@@ -173,13 +207,13 @@ sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_
   sage_status s;
   if ((s = check_tensor_args(q, "q")) || (s = check_tensor_args(k, "k")) || (s = check_tensor_args(v, "v"))) return s;
   const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
-  const bool empty = B * S * H == 0;
+  const bool empty = B == 0 || S == 0 || H == 0;
   if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "null output pointer");
   const size_t need = sage_prepare_workspace_bytes(B, S, H, q->size[3], smooth_k);
   if (!empty && need > 0 && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
   if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
-      (s = check_tensor_contract(v, "v", q->size)))
+      (s = check_tensor_contract(v, "v", q->size)) || (s = check_extent(B, S, H)))
     return s;
   const void* outs[] = {q8, q_scale, k8, k_scale, v8t, v_scale, k_mean, ws};
   for (const void* p : outs)
@@ -199,7 +233,7 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
   sage_status s;
   if ((s = check_sizes(B, S, H, D))) return s;
   if ((s = check_tensor_args(o, "o"))) return s;
-  const bool empty = B * S * H == 0;
+  const bool empty = B == 0 || S == 0 || H == 0;
   if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "null input pointer");
   if (want_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "null lse pointer");
@@ -207,7 +241,7 @@ static sage_status attn_impl(const int8_t* q8, const float* q_scale, const int8_
     return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   if (!sage::supported_head_dim(D)) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld is not 64 or 128", (long long)D);
   const int64_t want[4] = {B, S, H, D};
-  if ((s = check_tensor_contract(o, "o", want))) return s;
+  if ((s = check_tensor_contract(o, "o", want)) || (s = check_extent(B, S, H))) return s;
   const void* ins[] = {q8, q_scale, k8, k_scale, v8t, v_scale};
   for (const void* p : ins)
     if (p && !aligned16(p)) return fail(SAGE_ERR_UNSUPPORTED, "input pointer not 16-byte aligned");
@@ -250,13 +284,14 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
-  const bool empty = B * S * H == 0;
+  const bool empty = B == 0 || S == 0 || H == 0;
   const size_t need = sage_fused_workspace_bytes(B, S, H, q->size[3]);
   if (!empty && !ws) return fail(SAGE_ERR_INVALID_ARGUMENT, "null workspace");
   if (return_lse && !empty && !lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "return_lse set but lse is null");
   if (!return_lse && lse) return fail(SAGE_ERR_INVALID_ARGUMENT, "lse given but return_lse is 0");
   if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
-      (s = check_tensor_contract(v, "v", q->size)) || (s = check_tensor_contract(o, "o", q->size)))
+      (s = check_tensor_contract(v, "v", q->size)) || (s = check_tensor_contract(o, "o", q->size)) ||
+      (s = check_extent(B, S, H)))
     return s;
   if (ws && !aligned16(ws)) return fail(SAGE_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(SAGE_ERR_UNSUPPORTED, "lse not 4-byte aligned");

@@ -11,6 +11,9 @@ constexpr int kKvTile = 128;    // keys per online-softmax tile
 constexpr int kQBlock = 32;     // rows per INT8 quantization block
 constexpr int kChunk = 128;     // rows handled by one prologue workgroup pass
 constexpr int64_t kMaxSeq = int64_t(1) << 25;   // a head's quantized K or V (128 * S_pad bytes) stays below 4 GiB
+// B * H * S_pad / 128 bounds every launch's workgroup count (one per 128-row
+// chunk or query tile of a head); it must fit a 32-bit signed grid size.
+constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
 
 inline int64_t padded_len(int64_t S) { return S <= 0 ? 0 : (S + kKvTile - 1) / kKvTile * kKvTile; }
 

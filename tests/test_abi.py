@@ -128,6 +128,66 @@ def test_fused_validation_order_on_host():
     assert fused(h, causal=1, ws_bytes=10) == WS_SMALL
 
 
+def test_oversized_problems_are_refused_on_the_host():
+    """Sizes whose products overflow, problems with more workgroups than a
+    32-bit grid, and strides reaching past 2^60 elements are refused before any
+    device call (the workspace figure of such a problem is 0)."""
+    h = Host()
+    L = sage.lib()
+    huge = (1 << 40, 1 << 25, 1 << 40, 128)          # element count overflows int64
+    big = (1 << 20, 1 << 25, 1 << 10, 128)           # B*H*S/128 = 2^48 workgroups
+    t = h.tensor(big, stride=(8, 8, 8, 1))
+    for size, want in ((huge, INVALID), (big, UNSUPPORTED)):
+        q = h.tensor(size, stride=(8, 8, 8, 1))
+        assert fused(h, q=q, k=q, v=q, o=q, ws_bytes=1 << 62) == want, size
+        assert L.sage_fused_workspace_bytes(*size) == 0
+        assert L.sage_prepare_workspace_bytes(*size, 1) == 0
+    assert "too large" in (fused(h, q=t, k=t, v=t, o=t, ws_bytes=1 << 62) and last_error())
+    # sage_attn with the same sizes: o describes them, the extent check refuses
+    ptrs = [h.buf() for _ in range(6)]
+    o = h.tensor(big, stride=(8, 8, 8, 1))
+    assert L.sage_attn(*ptrs, *big[:3], 128, 0.1, ctypes.byref(o), None) == UNSUPPORTED
+    assert "too large" in last_error()
+    # the largest accepted grid is fine up to the device check
+    edge = (1, 1 << 25, 1 << 13, 128)                 # 2^13 heads x 2^18 tiles = 2^31 workgroups
+    ok_edge = (1, 1 << 25, (1 << 13) - 1, 128)
+    assert L.sage_fused_workspace_bytes(*edge) == 0 and L.sage_fused_workspace_bytes(*ok_edge) > 0
+    # strides that reach past 2^60 elements
+    far = h.tensor((4, 64, 2, 128), stride=(1 << 59, 256, 128, 1))
+    assert fused(h, q=far) == UNSUPPORTED and "2^60" in last_error()
+
+
+def test_random_descriptors_never_reach_the_device():
+    """Random descriptors (sizes, strides, dtypes, alignments, flags) on host
+    buffers: every call returns a documented status and none reaches a launch
+    (there is no GPU here, so success is only possible for an empty problem)."""
+    import random
+    rng = random.Random(20261202)
+    h = Host()
+    statuses = set()
+    for _ in range(3000):
+        size = [rng.choice([0, 1, 2, 3, 31, 64, 96, 128, 129, 1 << 20, 1 << 25, (1 << 25) + 1, 1 << 40, -1])
+                for _ in range(4)]
+        if rng.random() < 0.6:
+            size[3] = rng.choice([64, 128])
+        stride = [rng.choice([0, 1, 8, 16, 128, 256, 1 << 20, 1 << 59, 7, -8]) for _ in range(3)] + \
+                 [rng.choice([1, 1, 1, 2])]
+        q = sage.SageTensor(h.buf(misalign=rng.choice([0, 0, 0, 2])).value, rng.choice([1, 1, 1, 2]),
+                            (ctypes.c_int64 * 4)(*size), (ctypes.c_int64 * 4)(*stride))
+        other = q if rng.random() < 0.7 else h.tensor()
+        rc = fused(h, q=q, k=other, v=q, o=q, causal=rng.choice([0, 1]), sm=rng.choice([0.1, 0.0, float("nan")]),
+                   lse_flag=0, ws_bytes=rng.choice([0, 1 << 20, 1 << 62]))
+        statuses.add(rc)
+        assert rc in (OK, INVALID, UNSUPPORTED, WS_SMALL), rc
+        if rc == OK:
+            assert 0 in size[:3]
+        if rc == UNSUPPORTED and "device" in last_error().lower():
+            # everything up to the device check passed: the problem is within the limits
+            B, S, H, D = size
+            assert 0 < S <= 1 << 25 and D in (64, 128) and B * H * (-(-S // 128)) < 1 << 31
+    assert {INVALID, UNSUPPORTED} <= statuses
+
+
 def test_empty_problem_returns_ok_without_device():
     h = Host()
     z = (2, 0, 3, 128)
