@@ -445,6 +445,29 @@ def test_prepare_reuse_rewrites_the_same_buffers(sage):
         sage.prepare(*c, True, reuse=p)
 
 
+def test_calls_on_two_streams_at_once_match_serial_results(sage):
+    """The library keeps no state between calls: fused calls with their own
+    workspaces, issued alternately on two streams so that they overlap, give
+    the results of the same calls made one after another."""
+    import torch
+    ws_ = [synth.custom(1, 1000 + 37 * i, 4, smooth_k=bool(i % 2), base_seed=6400 + i) for i in range(4)]
+    data = [[to_dev(x) for x in inputs(w)] for w in ws_]
+    ref = [sage.sageattn(*d, is_causal=bool(i % 2), sm_scale=0.1, smooth_k=bool(i % 2)) for i, d in enumerate(data)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(d[0]) for d in data]
+    wss = [torch.empty(sage.fused_workspace_bytes(w.B, w.S, w.H, w.D), dtype=torch.uint8, device="cuda") for w in ws_]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for i, d in enumerate(data):
+            sage.sageattn(*d, is_causal=bool(i % 2), sm_scale=0.1, smooth_k=bool(i % 2), out=outs[i],
+                          workspace=wss[i], stream=streams[i % 2])
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), (rep, i)
+
+
 def test_hnd_layout_and_strided_output_match_nhd(sage):
     import torch
     w = synth.custom(2, 200, 3, smooth_k=True, base_seed=3100)
