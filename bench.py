@@ -113,6 +113,67 @@ def measure(w, steps: int, warmup: int, causal: bool = False):
     return dict(step_ms=step_ms_ev, step_wall_ms=wall_ms, attn_ms=attn_ms, prologue_ms=prep_ms)
 
 
+def one_call_at_a_time(w, calls: int, causal: bool = False):
+    """Each fused call timed alone: events around the call, synchronised before
+    the next one starts (no overlap with other calls). Median and minimum, ms."""
+    import torch
+    import quantized_attention_prepare_amd as sage
+    import synth
+
+    q, k, v = (to_dev(synth.tensor(w, x)) for x in "qkv")
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(q)
+    ws = torch.empty(sage.fused_workspace_bytes(w.B, w.S, w.H, w.D), dtype=torch.uint8, device=q.device)
+    ts = []
+    for i in range(calls + 20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sage.sageattn(q, k, v, "NHD", causal, w.sm_scale, False, w.smooth_k, out=out, workspace=ws, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        if i >= 20:   # warm-up calls
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4), "calls": calls}
+
+
+def cold_prologue(w, calls: int = 10):
+    """The prologue timed with the memory-side cache flushed before each call
+    (a 512 MiB buffer is written first, twice the cache): median and minimum, ms."""
+    import torch
+    import quantized_attention_prepare_amd as sage
+    import synth
+
+    q, k, v = (to_dev(synth.tensor(w, x)) for x in "qkv")
+    stream = torch.cuda.current_stream()
+    prep = sage.prepare(q, k, v, w.smooth_k, stream=stream)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    ts = []
+    for _ in range(calls):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sage.prepare(q, k, v, w.smooth_k, stream=stream, reuse=prep)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    del q, k, v, prep, flush
+    torch.cuda.empty_cache()
+    return {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4), "calls": calls}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The CPU oracle on a bounded sample of the workload: the prologue of one
     head plus as many of that head's query rows as fit the time budget."""
@@ -143,7 +204,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "sample": f"{w.name}: oracle prologue of head (0,0) ({w.S} rows, {t_prep:.2f} s, charged pro rata) + "
                       f"quantized attention of {rows_done} consecutive query rows of that head from a seeded start "
                       f"({t_attn:.2f} s); "
-                      f"{nthreads} threads"}
+                      f"{nthreads} threads on {cpu_model()}"}
 
 
 def main():
@@ -189,6 +250,8 @@ def main():
     value = fl / (r["step_ms"] * 1e-3) / 1e12
     achieved = fl / (r["attn_ms"] * 1e-3) / 1e12
     pro_bytes = prologue_compulsory_bytes(w)
+    cold = cold_prologue(w)
+    cold["gbs"] = round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1)
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         base, _, mode = name.partition(":")
@@ -202,6 +265,14 @@ def main():
                         "attn_tflops": round(fo / (ro["attn_ms"] * 1e-3) / 1e12, 1),
                         "prologue_ms": round(ro["prologue_ms"], 4),
                         "prologue_gbs": round(prologue_compulsory_bytes(wo) / (ro["prologue_ms"] * 1e-3) / 1e9, 1)}
+        # attention roofline: min(MFMA peak, arithmetic intensity x HBM peak) on 5 algorithmic bytes per element
+        ai = fo / (5.0 * wo.B * wo.S * wo.H * wo.D)
+        bound = min(MFMA_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+        others[name]["attn_roofline_tflops"] = round(bound, 1)
+        others[name]["attn_roofline_frac"] = round(fo / (ro["attn_ms"] * 1e-3) / 1e12 / bound, 4)
+        if base in ("C1", "C5") and not causal:
+            # short calls, each timed alone and synchronised before the next one
+            others[name]["one_call_at_a_time"] = one_call_at_a_time(wo, 200)
     line = {
         "metric": "attention TFLOPS (4*B*H*S^2*D/s) at H=28 D=128; prologue HBM GB/s",
         "value": round(value, 2),
@@ -224,7 +295,8 @@ def main():
                      "algorithmic_per_launch": f"{fl:.4e} ops (4*D ops per query-key pair)"},
         "prologue": {"ms": round(r["prologue_ms"], 4), "compulsory_bytes": pro_bytes,
                      "gbs": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "frac_of_hbm_peak": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "cold": cold},
         "step_wall_ms": round(r["step_wall_ms"], 4),
         "other_workloads": others,
     }

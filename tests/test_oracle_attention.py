@@ -6,7 +6,7 @@
  - a hand-worked case where P is not representable (RNE to E4M3 by hand) and
    one where a tiny probability underflows FP8 but still counts in l;
  - closed-form special cases (one key; all scores equal; V = 1 gives the
-   softmax row sum);
+   softmax row sum; one key far above the rest gives that key's value);
  - fp64 exact attention against torch's scaled_dot_product_attention in
    float64 (a library routine);
  - the quantized method against fp64 exact attention within an error bound
@@ -159,6 +159,30 @@ def test_underflowing_probability_counts_in_l_but_not_in_pv():
     h["v8t"][0, 1] = e4m3_code(448.0)
     ob, of = oracle.attn_rows_head(h, [0], unit_sm_scale(), T=128, want_f32=True)
     assert correctly_rounded_f32(of[0, 0], Fr(1) / (1 + Fr(1, 2 ** 20)))
+
+
+@pytest.mark.parametrize("jstar", [5, 200, 299])
+def test_one_hot_row_returns_that_keys_value(jstar):
+    # One key 30 log2 units (about 20.8 in natural log) above all others, with
+    # real V codes everywhere: the others' 448 * 2^-30 rounds to E4M3 zero once
+    # the maximum is known, so the row is that key's dequantized V; keys seen
+    # before it (p = 1 while their tile's maximum was 0) come in rescaled by
+    # 2^-30. |O - v*| <= 2^-30 (S max|v| + S |v*|) plus a few float roundings.
+    S = 300
+    h = make_head(S)
+    h["q8"][0, 0] = 1
+    h["k8"][jstar, 0] = 30
+    rng = np.random.default_rng(90 + jstar)
+    codes = rng.integers(0, 0x7F, size=(128, S)).astype(np.uint8) | (rng.integers(0, 2, size=(128, S)) << 7).astype(np.uint8)
+    h["v8t"][:, :S] = codes
+    ob, of = oracle.attn_rows_head(h, [0], unit_sm_scale(), T=128, want_f32=True)
+    dec = oracle.e4m3_decode_table()[h["v8t"][:, :S]].astype(np.float64)    # [D, S]
+    vstar = dec[:, jstar]
+    vmax = np.abs(dec).max(axis=1)
+    bound = 2.0 ** -30 * S * (vmax + np.abs(vstar)) + 4 * 2.0 ** -24 * np.abs(vstar) + 1e-30
+    assert np.all(np.abs(of[0].astype(np.float64) - vstar) <= bound)
+    # and it is not the plain mean: the other keys really are there
+    assert not np.allclose(vstar, dec.mean(axis=1))
 
 
 # ---------------------------------------------------------------- closed forms on prologue output
