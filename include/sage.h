@@ -29,8 +29,8 @@
  *          -> SAGE_ERR_INVALID_ARGUMENT;
  *       2. dtype other than BF16, D not 64 or 128, unequal shapes,
  *          stride[3] != 1, a base address / row stride that is not 16-byte
- *          aligned, strides reaching past 2^60 elements, S > 2^25
- *          (33,554,432 tokens), or B * H * ceil(S / 128) >= 2^31 (the
+ *          aligned, strides reaching past 2^60 elements, S > 2^25 - 128
+ *          (33,554,304 tokens), or B * H * ceil(S / 128) >= 2^31 (the
  *          workgroup count of a launch) -> SAGE_ERR_UNSUPPORTED;
  *       3. workspace smaller than the *_workspace_bytes() figure
  *          -> SAGE_ERR_WORKSPACE_TOO_SMALL;

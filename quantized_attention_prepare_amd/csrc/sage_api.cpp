@@ -54,7 +54,7 @@ bool extent_ok(int64_t B, int64_t S, int64_t H) {
 
 sage_status check_extent(int64_t B, int64_t S, int64_t H) {
   if (!extent_ok(B, S, H))
-    return fail(SAGE_ERR_UNSUPPORTED, "problem too large: B=%lld S=%lld H=%lld (S <= 2^25 and B*H*ceil(S/128) < 2^31)",
+    return fail(SAGE_ERR_UNSUPPORTED, "problem too large: B=%lld S=%lld H=%lld (S <= 2^25-128, B*H*ceil(S/128) < 2^31)",
                 (long long)B, (long long)S, (long long)H);
   return SAGE_OK;
 }
@@ -85,7 +85,7 @@ sage_status check_tensor_contract(const sage_tensor* t, const char* name, const 
                     (long long)t->size[i], (long long)ref_size[i]);
   if (t->stride[3] != 1) return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[3] must be 1", name);
   if (t->size[1] > sage::kMaxSeq)
-    return fail(SAGE_ERR_UNSUPPORTED, "%s: sequence length %lld exceeds 2^25", name, (long long)t->size[1]);
+    return fail(SAGE_ERR_UNSUPPORTED, "%s: sequence length %lld exceeds 2^25 - 128", name, (long long)t->size[1]);
   for (int i = 0; i < 3; ++i)
     if (t->stride[i] < 0 || (t->stride[i] % 8) != 0)
       return fail(SAGE_ERR_UNSUPPORTED, "%s: stride[%d]=%lld is not a non-negative multiple of 8 elements", name, i,

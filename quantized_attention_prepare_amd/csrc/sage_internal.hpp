@@ -10,7 +10,10 @@ inline bool supported_head_dim(int64_t D) { return D == 64 || D == 128; }
 constexpr int kKvTile = 128;    // keys per online-softmax tile
 constexpr int kQBlock = 32;     // rows per INT8 quantization block
 constexpr int kChunk = 128;     // rows handled by one prologue workgroup pass
-constexpr int64_t kMaxSeq = int64_t(1) << 25;   // a head's quantized K or V (128 * S_pad bytes) stays below 4 GiB
+// Longest sequence: a head's quantized K or V (S_pad * 128 bytes) must stay
+// below 4 GiB, the 32-bit byte extent of the attention kernel's buffer
+// resources; 2^25 - 128 rows is the largest whole number of key tiles under it.
+constexpr int64_t kMaxSeq = (int64_t(1) << 25) - kKvTile;
 // B * H * S_pad / 128 bounds every launch's workgroup count (one per 128-row
 // chunk or query tile of a head); it must fit a 32-bit signed grid size.
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;

@@ -135,7 +135,7 @@ def test_oversized_problems_are_refused_on_the_host():
     h = Host()
     L = sage.lib()
     huge = (1 << 40, 1 << 25, 1 << 40, 128)          # element count overflows int64
-    big = (1 << 20, 1 << 25, 1 << 10, 128)           # B*H*S/128 = 2^48 workgroups
+    big = (1 << 20, 1 << 24, 1 << 10, 128)           # B*H*S/128 = 2^47 workgroups
     t = h.tensor(big, stride=(8, 8, 8, 1))
     for size, want in ((huge, INVALID), (big, UNSUPPORTED)):
         q = h.tensor(size, stride=(8, 8, 8, 1))
@@ -149,9 +149,18 @@ def test_oversized_problems_are_refused_on_the_host():
     assert L.sage_attn(*ptrs, *big[:3], 128, 0.1, ctypes.byref(o), None) == UNSUPPORTED
     assert "too large" in last_error()
     # the largest accepted grid is fine up to the device check
-    edge = (1, 1 << 25, 1 << 13, 128)                 # 2^13 heads x 2^18 tiles = 2^31 workgroups
-    ok_edge = (1, 1 << 25, (1 << 13) - 1, 128)
+    smax = (1 << 25) - 128                           # longest sequence: S_pad * 128 bytes < 4 GiB
+    edge = (1, smax, (1 << 13) + 1, 128)             # (2^13 + 1) heads x (2^18 - 1) tiles > 2^31 - 1 workgroups
+    ok_edge = (1, smax, 1 << 13, 128)                # 2^31 - 2^13 workgroups
     assert L.sage_fused_workspace_bytes(*edge) == 0 and L.sage_fused_workspace_bytes(*ok_edge) > 0
+    # S = 2^25 would give a 2^32-byte head, past the kernel's 32-bit buffer extent
+    for D in (64, 128):
+        assert L.sage_fused_workspace_bytes(1, smax, 1, D) > 0 and L.sage_fused_workspace_bytes(1, smax + 1, 1, D) == 0
+        o_max = h.tensor((1, smax + 1, 1, D), stride=(8, 8, 8, 1))
+        assert L.sage_attn(*ptrs, 1, smax + 1, 1, D, 0.1, ctypes.byref(o_max), None) == UNSUPPORTED
+        o_ok = h.tensor((1, smax, 1, D), stride=(8, 8, 8, 1))
+        assert L.sage_attn(*ptrs, 1, smax, 1, D, 0.1, ctypes.byref(o_ok), None) == UNSUPPORTED
+        assert "device" in last_error().lower()
     # strides that reach past 2^60 elements
     far = h.tensor((4, 64, 2, 128), stride=(1 << 59, 256, 128, 1))
     assert fused(h, q=far) == UNSUPPORTED and "2^60" in last_error()
@@ -166,7 +175,8 @@ def test_random_descriptors_never_reach_the_device():
     h = Host()
     statuses = set()
     for _ in range(3000):
-        size = [rng.choice([0, 1, 2, 3, 31, 64, 96, 128, 129, 1 << 20, 1 << 25, (1 << 25) + 1, 1 << 40, -1])
+        size = [rng.choice([0, 1, 2, 3, 31, 64, 96, 128, 129, 1 << 20, (1 << 25) - 128, (1 << 25) - 127, 1 << 25,
+                            1 << 40, -1])
                 for _ in range(4)]
         if rng.random() < 0.6:
             size[3] = rng.choice([64, 128])
@@ -184,7 +194,7 @@ def test_random_descriptors_never_reach_the_device():
         if rc == UNSUPPORTED and "device" in last_error().lower():
             # everything up to the device check passed: the problem is within the limits
             B, S, H, D = size
-            assert 0 < S <= 1 << 25 and D in (64, 128) and B * H * (-(-S // 128)) < 1 << 31
+            assert 0 < S <= (1 << 25) - 128 and D in (64, 128) and B * H * (-(-S // 128)) < (1 << 31) - 1
     assert {INVALID, UNSUPPORTED} <= statuses
 
 
