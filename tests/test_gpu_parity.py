@@ -33,10 +33,13 @@ def sage():
     import quantized_attention_prepare_amd as s
     s.lib()
     yield s
-    os.makedirs("gpurun_out", exist_ok=True)
-    with open("gpurun_out/parity_results.jsonl", "a") as f:
-        for r in RESULTS:
-            f.write(json.dumps(r) + "\n")
+    # the per-case metrics go to SAGE_PARITY_OUT (a JSON-lines file) when it is set
+    path = os.environ.get("SAGE_PARITY_OUT")
+    if path:
+        os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
+        with open(path, "a") as f:
+            for r in RESULTS:
+                f.write(json.dumps(r) + "\n")
 
 
 def to_dev(bits: np.ndarray):
