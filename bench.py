@@ -41,12 +41,25 @@ def prologue_compulsory_bytes(w) -> int:
     return 9 * n + 2 * 4 * blocks + 4 * w.B * w.H * w.D * (2 if w.smooth_k else 1)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(main: str = "attention.hip") -> str:
+    """First 16 hex digits of sha256 over a kernel source and the shared internal header."""
     h = hashlib.sha256()
-    for f in ("attention.hip", "sage_internal.hpp"):
+    for f in (main, "sage_internal.hpp"):
         with open(os.path.join(ROOT, "quantized_attention_prepare_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def load_prologue_traffic(workload: str):
+    """HBM bytes of one prologue call (its three kernels) from committed counters, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"prologue_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("prologue_source_sha") != kernel_source_hash("prologue.hip"):
+        return None
+    return rec.get("traffic_bytes_per_call")
 
 
 def load_traffic(workload: str):
@@ -250,6 +263,7 @@ def main():
     value = fl / (r["step_ms"] * 1e-3) / 1e12
     achieved = fl / (r["attn_ms"] * 1e-3) / 1e12
     pro_bytes = prologue_compulsory_bytes(w)
+    pro_traffic = load_prologue_traffic(w.name)
     cold = cold_prologue(w)
     cold["gbs"] = round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1)
     others = {}
@@ -296,6 +310,11 @@ def main():
         "prologue": {"ms": round(r["prologue_ms"], 4), "compulsory_bytes": pro_bytes,
                      "gbs": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": pro_traffic,
+                     "achieved_gbs": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9, 1)
+                                      if pro_traffic else None),
+                     "achieved_frac_of_hbm_peak": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                                   if pro_traffic else None),
                      "cold": cold},
         "step_wall_ms": round(r["step_wall_ms"], 4),
         "other_workloads": others,
