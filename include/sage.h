@@ -86,7 +86,8 @@ typedef struct {
  * result: P is requantized against the running maximum after each tile. */
 int sage_kv_tile(void);
 
-/* S rounded up to a multiple of sage_kv_tile(); 0 for S <= 0. */
+/* S rounded up to a multiple of sage_kv_tile(); 0 for S <= 0, -1 when the
+ * rounded value does not fit in int64. */
 int64_t sage_padded_len(int64_t S);
 
 /* Device workspace sage_prepare needs (per-chunk channel statistics); 0 for

@@ -18,7 +18,12 @@ constexpr int64_t kMaxSeq = (int64_t(1) << 25) - kKvTile;
 // chunk or query tile of a head); it must fit a 32-bit signed grid size.
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
 
-inline int64_t padded_len(int64_t S) { return S <= 0 ? 0 : (S + kKvTile - 1) / kKvTile * kKvTile; }
+// S rounded up to whole key tiles; 0 for S <= 0, -1 when that does not fit int64.
+inline int64_t padded_len(int64_t S) {
+  if (S <= 0) return 0;
+  const int64_t tiles = S / kKvTile + (S % kKvTile != 0);
+  return tiles > INT64_MAX / kKvTile ? -1 : tiles * kKvTile;
+}
 
 // Strided BF16 input view: element (b, s, h, d) at data[b*sb + s*ss + h*sh + d].
 struct Bf16View {

@@ -32,6 +32,8 @@ def test_library_exports_every_declared_function():
 def test_constants_and_sizes():
     assert sage.kv_tile() == 128
     assert [sage.padded_len(s) for s in (0, 1, 128, 129, 300)] == [0, 128, 128, 256, 384]
+    assert sage.padded_len(2 ** 63 - 1) == -1 and sage.padded_len(2 ** 63 - 128) == 2 ** 63 - 128
+    assert sage.padded_len(-5) == 0
     L = sage.lib()
     assert L.sage_fused_workspace_bytes(0, 10, 2, 128) == 0
     small = L.sage_fused_workspace_bytes(1, 256, 2, 128)

@@ -485,6 +485,73 @@ def test_calls_on_two_streams_at_once_match_serial_results(sage):
             assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), (rep, i)
 
 
+def test_outputs_leave_guard_bands_untouched(sage):
+    """Every output buffer sits inside a larger allocation filled with a
+    canary byte: after prepare, attn (with the log-sum-exp) and the fused call,
+    causal and not, on ragged shapes at both head dims, the canary bytes on
+    either side are unchanged (and the outputs are those of ordinary calls)."""
+    import ctypes
+    import torch
+    G = 4096   # guard bytes on each side
+    for (B, S, H, D) in ((2, 300, 3, 128), (1, 129, 2, 64), (3, 33, 1, 128)):
+        w = synth.custom(B, S, H, D=D, smooth_k=True, base_seed=6500 + S)
+        q, k, v = (to_dev(x) for x in inputs(w))
+        Sp = sage.padded_len(S)
+        L = sage.lib()
+        shapes = dict(q8=(B * H * Sp * D, 1), q_scale=(B * H * Sp // 32, 4), k8=(B * H * Sp * D, 1),
+                      k_scale=(B * H * Sp // 32, 4), v8t=(B * H * D * Sp, 1), v_scale=(B * H * D, 4),
+                      k_mean=(B * H * D, 4), out=(B * S * H * D, 2), lse=(B * H * S, 4))
+        bufs = {}
+        for name, (n, item) in shapes.items():
+            raw = torch.full((n * item + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+            bufs[name] = raw
+        def inner(name):
+            n, item = shapes[name]
+            return bufs[name][G:G + n * item]
+        nws = L.sage_prepare_workspace_bytes(B, S, H, D, 1)
+        wsraw = torch.full((nws + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+        tq, tk, tv = sage.describe(q), sage.describe(k), sage.describe(v)
+        P = sage._ptr
+        sage.check(L.sage_prepare(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), 1, P(inner("q8")),
+                                  P(inner("q_scale")), P(inner("k8")), P(inner("k_scale")), P(inner("v8t")),
+                                  P(inner("v_scale")), P(inner("k_mean")), P(wsraw[G:G + nws]), nws, sage._stream(None)))
+        out = inner("out").view(torch.bfloat16).view(B, S, H, D)
+        to = sage.describe(out)
+        for causal in (0, 1):
+            sage.check(L.sage_attn_ex(P(inner("q8")), P(inner("q_scale")), P(inner("k8")), P(inner("k_scale")),
+                                      P(inner("v8t")), P(inner("v_scale")), B, S, H, D, 0.1, causal, ctypes.byref(to),
+                                      P(inner("lse")), sage._stream(None)))
+            torch.cuda.synchronize()
+            ref = sage.sageattn(q, k, v, is_causal=bool(causal), sm_scale=0.1, return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
+            assert torch.equal(inner("lse").view(torch.float32).view(B, H, S), ref[1])
+        # the fused call into a guarded output, with a guarded workspace
+        nf = sage.fused_workspace_bytes(B, S, H, D)
+        fws = torch.full((nf + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+        oraw = torch.full((B * S * H * D * 2 + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+        fo = oraw[G:G + B * S * H * D * 2].view(torch.bfloat16).view(B, S, H, D)
+        sage.sageattn(q, k, v, sm_scale=0.1, out=fo, workspace=fws[G:G + nf])
+        torch.cuda.synchronize()
+        for name, raw in list(bufs.items()) + [("ws", wsraw), ("fused_ws", fws), ("fused_out", oraw)]:
+            head, tail = raw[:G], raw[-G:]
+            assert bool((head == 0xA5).all()) and bool((tail == 0xA5).all()), (B, S, H, D, name)
+
+
+def test_v_times_a_power_of_two_scales_the_output_exactly(sage):
+    """V * 2^k scales each channel's amax, hence v_scale, by 2^k and leaves the
+    FP8 codes as they are, so the output is multiplied by 2^k bit for bit."""
+    import torch
+    w = synth.custom(2, 500, 3, smooth_k=True, base_seed=6600)
+    q, k, v = (to_dev(x) for x in inputs(w))
+    for causal in (False, True):
+        o1 = sage.sageattn(q, k, v, is_causal=causal, sm_scale=w.sm_scale)
+        for e in (-3, 2, 5):
+            o2 = sage.sageattn(q, k, v * (2.0 ** e), is_causal=causal, sm_scale=w.sm_scale)
+            torch.cuda.synchronize()
+            assert torch.equal((o1.float() * 2.0 ** e).to(torch.bfloat16).view(torch.int16), o2.view(torch.int16)), e
+
+
 def test_hnd_layout_and_strided_output_match_nhd(sage):
     import torch
     w = synth.custom(2, 200, 3, smooth_k=True, base_seed=3100)
