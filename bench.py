@@ -317,6 +317,7 @@ def main():
                                                    if pro_traffic else None),
                      "cold": cold},
         "step_wall_ms": round(r["step_wall_ms"], 4),
+        "one_call_at_a_time": one_call_at_a_time(w, 10),
         "other_workloads": others,
     }
     if not args.no_cpu:
