@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -42,11 +43,15 @@ def prologue_compulsory_bytes(w) -> int:
 
 
 def kernel_source_hash(main: str = "attention.hip") -> str:
-    """First 16 hex digits of sha256 over a kernel source and the shared internal header."""
+    """First 16 hex digits of sha256 over the code (comments and whitespace removed) of a
+    kernel source and the shared internal header: a comment edit keeps the hash."""
     h = hashlib.sha256()
     for f in (main, "sage_internal.hpp"):
-        with open(os.path.join(ROOT, "quantized_attention_prepare_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_attention_prepare_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

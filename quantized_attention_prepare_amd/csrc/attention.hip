@@ -10,13 +10,14 @@
 //   uniform per wave. Keys are consumed in tiles of 128 (the online-softmax
 //   tile, part of the result's definition).
 //
-// Schedule (per wave, iteration t)
-//   max of tile t's scores -> issue the INT8 score MFMAs of tile t+1 (their
-//   results are not needed until the next iteration) -> exp2 / FP8 packing of
-//   tile t while those MFMAs execute -> rescale O -> issue the FP8 PV MFMAs of
-//   tile t, which run on into the next iteration's copy wait and max. The
-//   matrix cores thus work under the same wave's softmax; the other workgroup
-//   on the CU, unsynchronised with this one, fills the remaining gaps.
+// Schedule (per wave, iteration t: a fixed sequence of slots, one MFMA each)
+//   the FP8 PV MFMAs of tile t-1 issue under the maximum of tile t's scores
+//   and its first exp2 / FP8 groups; then the INT8 score MFMAs of tile t+1
+//   (not needed before the next iteration) issue under the remaining exp2
+//   groups, the update of l and the rescale of O. The matrix cores thus work
+//   under the same wave's softmax; the other workgroup on the CU,
+//   unsynchronised with this one, fills the remaining gaps. Causal attention
+//   stops at the key tile of the workgroup's own queries and masks it per lane.
 //
 // MFMA data flow (lane l, half h = l / 32, query column l % 32)
 //   scores as S^T = K . Q^T with v_mfma_i32_32x32x32_i8: A = K rows, B = Q^T.
