@@ -146,6 +146,25 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _gpu_of(*tensors, stream=None) -> int:
+    """Index of the one GPU every given tensor (and the stream) lives on; the
+    library takes device pointers, so a host tensor or a mix of devices is an
+    error here rather than a fault on the device."""
+    idx = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on a GPU: the library takes device pointers")
+        if idx is None:
+            idx = t.device.index
+        elif t.device.index != idx:
+            raise ValueError(f"tensors on different GPUs ({idx} and {t.device.index})")
+    if stream is not None and idx is not None and stream.device.index != idx:
+        raise ValueError(f"the stream belongs to GPU {stream.device.index}, the tensors to GPU {idx}")
+    return idx
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -156,6 +175,14 @@ def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None, re
     reuse: the dict a previous prepare() returned for the same B, S, H, D; its
     tensors and workspace are written again instead of allocating new ones.
     """
+    import torch
+    reused = [reuse[key] for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale", "k_mean", "_ws")] \
+        if reuse is not None else []
+    with torch.cuda.device(_gpu_of(q, k, v, *reused, stream=stream)):
+        return _prepare(q, k, v, smooth_k, layout, stream, reuse)
+
+
+def _prepare(q, k, v, smooth_k, layout, stream, reuse):
     import torch
     tq, tk, tv = describe(q, layout), describe(k, layout), describe(v, layout)
     B, S, H, D = tq.size
@@ -191,6 +218,13 @@ def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = 
     return_lse also the rows' log-sum-exp, float32 [B, H, S] (sage_attn_lse).
     is_causal: query i sees keys 0 .. i (sage_attn_ex)."""
     import torch
+    tensors = [prep[key] for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale")]
+    with torch.cuda.device(_gpu_of(*tensors, out, lse, stream=stream)):
+        return _attn(prep, sm_scale, out, stream, return_lse, lse, is_causal)
+
+
+def _attn(prep, sm_scale, out, stream, return_lse, lse, is_causal):
+    import torch
     B, H, Sp, D = prep["q8"].shape
     S = prep["S"]
     if out is None:
@@ -223,6 +257,12 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
     returns the rows' log-sum-exp of the dequantized scores, float32 [B, H, S]
     (both extensions: the pages' sageattn rejects them).
     """
+    import torch
+    with torch.cuda.device(_gpu_of(q, k, v, out, workspace, stream=stream)):
+        return _sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse, smooth_k, out, workspace, stream)
+
+
+def _sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse, smooth_k, out, workspace, stream):
     import torch
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])

@@ -270,3 +270,17 @@ def test_python_binding_raises_typed_errors():
         sage.check(WS_SMALL)
     with pytest.raises(RuntimeError):
         sage.check(DEVICE)
+
+
+def test_binding_refuses_host_tensors_before_any_library_call():
+    """The library takes device pointers; the binding turns host tensors into an
+    error (a host pointer reaching a kernel would fault the GPU)."""
+    import torch
+    q = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sage.sageattn(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        sage.prepare(q, q, q)
+    prep = {key: torch.zeros(4) for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale")}
+    with pytest.raises(ValueError, match="GPU"):
+        sage.attn(prep, 0.1)
