@@ -97,7 +97,7 @@ def time_events(fn, iters: int, stream) -> float:
     return start.elapsed_time(end) / iters
 
 
-def measure(w, steps: int, warmup: int, causal: bool = False):
+def measure(w, steps: int, warmup: int, causal: bool = False, keep_head: bool = False):
     import torch
     import quantized_attention_prepare_amd as sage
     import synth
@@ -126,9 +126,11 @@ def measure(w, steps: int, warmup: int, causal: bool = False):
     attn_ms = time_events(lambda: sage.attn(prep, w.sm_scale, out=o2, stream=stream, is_causal=causal), steps, stream)
     prep_ms = time_events(lambda: sage.prepare(q, k, v, w.smooth_k, stream=stream, reuse=prep), steps, stream)
     torch.cuda.synchronize()
+    # the output rows of head (0, 0) from the last timed step, for the CPU leg's accuracy check
+    head = out[0, :, 0, :].contiguous().view(torch.int16).cpu().numpy() if keep_head else None
     del q, k, v, out, ws, prep, o2
     torch.cuda.empty_cache()
-    return dict(step_ms=step_ms_ev, step_wall_ms=wall_ms, attn_ms=attn_ms, prologue_ms=prep_ms)
+    return dict(step_ms=step_ms_ev, step_wall_ms=wall_ms, attn_ms=attn_ms, prologue_ms=prep_ms, head=head)
 
 
 def one_call_at_a_time(w, calls: int, causal: bool = False):
@@ -192,9 +194,11 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
+def cpu_baseline(w, budget_s: float = 12.0, gpu_head=None):
     """The CPU oracle on a bounded sample of the workload: the prologue of one
-    head plus as many of that head's query rows as fit the time budget."""
+    head plus as many of that head's query rows as fit the time budget. With
+    gpu_head (the GPU's BF16 output bits of head (0, 0), [S, D]) it also
+    returns the GPU's error on the rows the oracle computed."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
@@ -209,16 +213,26 @@ def cpu_baseline(w, budget_s: float = 12.0):
     rows_done = 0
     t_attn = 0.0
     start = int(synth.sample_rows(w, 1)[0, 2])
+    rows, bits = [], []
     with ThreadPoolExecutor(nthreads) as ex:
         while t_attn < budget_s and rows_done < w.S:
             batch = [(start + rows_done + i) % w.S for i in range(nthreads)]
             t1 = time.perf_counter()
-            list(ex.map(lambda r: oracle.attn_rows_head(prep, [r], w.sm_scale), batch))
+            res = list(ex.map(lambda r: oracle.attn_rows_head(prep, [r], w.sm_scale), batch))
             t_attn += time.perf_counter() - t1
             rows_done += len(batch)
+            rows += batch
+            bits += res
     ops = 4.0 * rows_done * w.S * w.D
     t_share = t_prep * rows_done / w.S
-    return {"value": ops / (t_attn + t_share) / 1e12, "unit": "TFLOPS", "cores": nthreads, "kind": "oracle",
+    accuracy = None
+    if gpu_head is not None:
+        ref = oracle.bf16_bits_to_f64(np.concatenate(bits).astype(np.uint16))
+        got = oracle.bf16_bits_to_f64(gpu_head.view(np.uint16)[np.array(rows)])
+        accuracy = {"rows": len(rows), "head": "(0, 0)", "maxabs_vs_oracle": round(oracle.max_abs_rel(got, ref), 6),
+                    "cos_vs_oracle": round(oracle.cosine(got, ref), 8),
+                    "bits_equal_frac": round(float(np.mean(got == ref)), 4)}
+    return accuracy, {"value": ops / (t_attn + t_share) / 1e12, "unit": "TFLOPS", "cores": nthreads, "kind": "oracle",
             "sample": f"{w.name}: oracle prologue of head (0,0) ({w.S} rows, {t_prep:.2f} s, charged pro rata) + "
                       f"quantized attention of {rows_done} consecutive query rows of that head from a seeded start "
                       f"({t_attn:.2f} s); "
@@ -263,7 +277,7 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    r = measure(w, args.steps, args.warmup)
+    r = measure(w, args.steps, args.warmup, keep_head=not args.no_cpu)
     fl = attn_flops(w)
     value = fl / (r["step_ms"] * 1e-3) / 1e12
     achieved = fl / (r["attn_ms"] * 1e-3) / 1e12
@@ -326,7 +340,8 @@ def main():
         "other_workloads": others,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w)
+        accuracy, line["cpu_baseline"] = cpu_baseline(w, gpu_head=r["head"])
+        line["accuracy_vs_oracle"] = accuracy
     print(json.dumps(line), flush=True)
 
 
