@@ -351,6 +351,41 @@ def test_causal_workload_rows(sage, name, n):
     check_lse(f"causal_lse_{name}", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
 
 
+# ------------------------------------------------------------------ randomized sweep
+def _random_cases(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        S = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 300)), int(rng.integers(300, 700))]))
+        cases.append((i, int(rng.integers(1, 4)), S, int(rng.integers(1, 5)), int(rng.choice([64, 128])),
+                      bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), str(rng.choice(["NHD", "HND"]))))
+    return cases
+
+
+@pytest.mark.parametrize("i,B,S,H,D,smooth_k,causal,layout", _random_cases())
+def test_random_configurations_against_the_oracle(sage, i, B, S, H, D, smooth_k, causal, layout):
+    """Seeded random shapes (B <= 3, S < 700, H <= 4), head dims, smooth_k,
+    causal and layouts: prologue bit for bit, output and log-sum-exp within
+    tolerance, against the oracle on every row."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=7100 + i)
+    q, k, v = inputs(w)
+    o = oracle.prepare(q, k, v, smooth_k)
+    check_prologue(gpu_prepare(sage, q, k, v, smooth_k), o, S, smooth_k=smooth_k)
+    tq, tk, tv = (to_dev(x) for x in (q, k, v))
+    if layout == "HND":
+        tq, tk, tv = (x.permute(0, 2, 1, 3).contiguous() for x in (tq, tk, tv))
+    out, lse = sage.sageattn(tq, tk, tv, layout, causal, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    if layout == "HND":
+        out = out.permute(0, 2, 1, 3).contiguous()
+    R, lse_o = oracle.attn(o, w.sm_scale, want_lse=True, causal=causal)
+    E = oracle.exact(q, k, v, w.sm_scale, causal=causal)
+    compare_attention(f"random{i}_{B}x{S}x{H}x{D}_{'sk' if smooth_k else 'nosk'}_{'c' if causal else 'nc'}_{layout}",
+                      out.view(torch.int16).cpu().numpy().view(np.uint16), R, E)
+    check_lse(f"random{i}_lse", lse.cpu().numpy(), lse_o)
+
+
 # ------------------------------------------------------------------ 64-bit offsets, graph capture
 def test_tensors_past_2_31_elements(sage):
     """B*S*H*D = 3*65536*96*128 > 2^31 elements (4.8 GB per BF16 tensor): the
