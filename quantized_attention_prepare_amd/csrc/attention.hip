@@ -233,14 +233,15 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
 // each slot holding at most one MFMA and a run of VALU work that issues while
 // the MFMA executes:
 //   slots 1-8   PV of the previous tile (its probabilities in pk, its V tile in
-//               vbuf_prev), with the maximum of this tile's scores and then the
-//               exp2 of blocks 0 and 1 (whose FP8 codes go to pk[0] once the
-//               MFMAs that read the previous pk[0] have been issued);
+//               vbuf_prev), with the maximum of this tile's scores (one block
+//               per slot) and then the exp2 of blocks 0 and 1 (whose FP8 codes
+//               go to pk[0] once the MFMAs that read the previous pk[0] have
+//               been issued);
 //   slots 9-24  the INT8 score MFMAs of the next tile, with the exp2 of blocks
 //               2 and 3, l, and the rescale of O (the previous PV is complete by
 //               then).
 // At D = 64 there are four PV and eight score MFMAs, two exp2 groups per slot.
-// The LDS operands of each MFMA are read one slot ahead. kHasPrev is false for
+// The LDS operands of each MFMA are read two slots ahead. kHasPrev is false for
 // the first tile. cblk[kb] = (q_scale * k_scale) * sm_scale * log2 e of the
 // tile's 32-key blocks. nvalid < 128 marks a ragged last tile: padded keys'
 // scores become INT32_MIN (below every valid score since |acc| <= 2^21), blocks
@@ -262,9 +263,18 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
   const int fq = Dim<D>::fq(col);    // Q swizzle of row col
   const int fv = (col >> 1) & 7;     // V swizzle of rows 32 d + col
   const uint8_t* krow = kbuf_next + prow * D;
-  // ---- slot 0: first V operand; tail masking; max of blocks 0, 1
-  v8i vop;
-  if (kHasPrev) vop = v_operand(vbuf_prev, 0, 0, half, col, fv);
+  // ---- slot 0: first two V operands; tail masking; max of block 0
+  // Operands are read two slots ahead into alternating registers (one slot of
+  // VALU work is often shorter than an LDS read): PV MFMA P reads vv[P & 1],
+  // score MFMA Q reads kk[Q & 1] and qq[(Q / 4) & 1].
+  constexpr int NPV = 2 * Dim<D>::kOBlk;          // PV MFMAs (kc outer, d inner)
+  constexpr int NQK = 4 * Dim<D>::kSteps;         // score MFMAs (s outer, kb inner)
+  v8i vv[2];
+  v4i kk[2], qq[2];
+  if (kHasPrev) {
+    vv[0] = v_operand(vbuf_prev, 0, 0, half, col, fv);
+    vv[1] = v_operand(vbuf_prev, 1 / Dim<D>::kOBlk, 1 % Dim<D>::kOBlk, half, col, fv);
+  }
   if (masked) {
     // Only the last tile gets here. The empty asm hides that nvalid is then
     // the loop-invariant length of the last tile, which would otherwise move
@@ -280,22 +290,31 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
         sc[kb][v] = (sc[kb][v] & keep) | (INT32_MIN & ~keep);
       }
   }
-  float tmax = fmaxf(block_max(sc[0], cblk[0]), block_max(sc[1], cblk[1]));
+  float tmax = block_max(sc[0], cblk[0]);
   SAGE_FENCE();
-#define SAGE_PV_SLOT(KC_, D_, NKC_, ND_, WORK_)                                                            \
-  {                                                                                                         \
-    if (kHasPrev) {                                                                                         \
-      st.oacc[D_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, st.pk[KC_], st.oacc[D_], 0, 0, 0, \
-                                                                    0, 0, 0);                               \
-      if ((NKC_) >= 0) vop = v_operand(vbuf_prev, NKC_, ND_, half, col, fv);                                \
-    }                                                                                                       \
-    WORK_;                                                                                                  \
-    SAGE_FENCE();                                                                                           \
+#define SAGE_KOP(Q_) (*reinterpret_cast<const v4i*>(krow + 32 * ((Q_) % 4) * D + (((2 * ((Q_) / 4) + half) ^ fk) * 16)))
+#define SAGE_QOP(S_) (*reinterpret_cast<const v4i*>(qrow + (((2 * (S_) + half) ^ fq) * 16)))
+#define SAGE_PV_SLOT(P_, WORK_)                                                                              \
+  {                                                                                                           \
+    if (kHasPrev) {                                                                                           \
+      constexpr int kc_ = (P_) / Dim<D>::kOBlk, d_ = (P_) % Dim<D>::kOBlk;                                    \
+      st.oacc[d_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv[(P_) & 1], st.pk[kc_], st.oacc[d_], 0, \
+                                                                    0, 0, 0, 0, 0);                           \
+      if ((P_) + 2 < NPV)                                                                                     \
+        vv[(P_) & 1] = v_operand(vbuf_prev, ((P_) + 2) / Dim<D>::kOBlk, ((P_) + 2) % Dim<D>::kOBlk, half, col, \
+                                 fv);                                                                         \
+    }                                                                                                         \
+    if ((P_) == NPV - 2) {                                                                                    \
+      qq[0] = SAGE_QOP(0);                                                                                    \
+      kk[0] = SAGE_KOP(0);                                                                                    \
+    }                                                                                                         \
+    if ((P_) == NPV - 1) kk[1] = SAGE_KOP(1);                                                                 \
+    WORK_;                                                                                                    \
+    SAGE_FENCE();                                                                                             \
   }
   float m_new, alpha, moff;
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #define SAGE_EXP(KB_, G_) exp_group(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
-  v4i qop, kop;
 #define SAGE_L_UPDATE()                                                                               \
   {                                                                                                   \
     float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                   \
@@ -310,85 +329,80 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
     st.m_run = m_new;                                                                                 \
   }
   if constexpr (D == 128) {
-  SAGE_PV_SLOT(0, 0, 0, 1, tmax = fmaxf(tmax, fmaxf(block_max(sc[2], cblk[2]), block_max(sc[3], cblk[3]))))
-  SAGE_PV_SLOT(0, 1, 0, 2, {
+  SAGE_PV_SLOT(0, tmax = fmaxf(tmax, block_max(sc[1], cblk[1])))
+  SAGE_PV_SLOT(1, tmax = fmaxf(tmax, block_max(sc[2], cblk[2])))
+  SAGE_PV_SLOT(2, tmax = fmaxf(tmax, block_max(sc[3], cblk[3])))
+  SAGE_PV_SLOT(3, {
     tmax = max_xor32(tmax);
     m_new = fmaxf(st.m_run, tmax);
     alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
     moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
   })
-  SAGE_PV_SLOT(0, 2, 0, 3, (void)0)
-  SAGE_PV_SLOT(0, 3, 1, 0, (void)0)
   // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
-  SAGE_PV_SLOT(1, 0, 1, 1, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
-  SAGE_PV_SLOT(1, 1, 1, 2, { SAGE_EXP(0, 2); SAGE_EXP(0, 3); })
-  SAGE_PV_SLOT(1, 2, 1, 3, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
-  qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
-  SAGE_PV_SLOT(1, 3, -1, 0, {
-    kop = *reinterpret_cast<const v4i*>(krow + (((0 + half) ^ fk) * 16));
-    SAGE_EXP(1, 2);
-    SAGE_EXP(1, 3);
-  })
+  SAGE_PV_SLOT(4, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
+  SAGE_PV_SLOT(5, { SAGE_EXP(0, 2); SAGE_EXP(0, 3); })
+  SAGE_PV_SLOT(6, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
+  SAGE_PV_SLOT(7, { SAGE_EXP(1, 2); SAGE_EXP(1, 3); })
   } else {
-  SAGE_PV_SLOT(0, 0, 0, 1, tmax = fmaxf(tmax, fmaxf(block_max(sc[2], cblk[2]), block_max(sc[3], cblk[3]))))
-  SAGE_PV_SLOT(0, 1, 1, 0, {
+  SAGE_PV_SLOT(0, tmax = fmaxf(tmax, fmaxf(block_max(sc[1], cblk[1]), block_max(sc[2], cblk[2]))))
+  SAGE_PV_SLOT(1, {
+    tmax = fmaxf(tmax, block_max(sc[3], cblk[3]));
     tmax = max_xor32(tmax);
     m_new = fmaxf(st.m_run, tmax);
     alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
     moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
   })
   // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
-  SAGE_PV_SLOT(1, 0, 1, 1, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
-  qop = *reinterpret_cast<const v4i*>(qrow + (((0 + half) ^ fq) * 16));
-  SAGE_PV_SLOT(1, 1, -1, 0, {
-    kop = *reinterpret_cast<const v4i*>(krow + (((0 + half) ^ fk) * 16));
-    SAGE_EXP(0, 2);
-    SAGE_EXP(0, 3);
-  })
+  SAGE_PV_SLOT(2, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
+  SAGE_PV_SLOT(3, { SAGE_EXP(0, 2); SAGE_EXP(0, 3); })
   }
 #undef SAGE_PV_SLOT
   // ---- score MFMAs of the next tile (s outer, kb inner)
-#define SAGE_QK_SLOT(S_, KB_, NS_, NKB_, WORK_)                                                         \
-  {                                                                                                      \
-    const v16i z = {};                                                                                   \
-    snext[KB_] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop, (S_) == 0 ? z : snext[KB_], 0, 0, 0);   \
-    if ((NS_) >= 0) {                                                                                    \
-      if ((NS_) != (S_)) qop = *reinterpret_cast<const v4i*>(qrow + (((2 * (NS_) + half) ^ fq) * 16));   \
-      kop = *reinterpret_cast<const v4i*>(krow + 32 * (NKB_) * D + (((2 * (NS_) + half) ^ fk) * 16));  \
-    }                                                                                                    \
-    WORK_;                                                                                               \
-    SAGE_FENCE();                                                                                        \
+#define SAGE_QK_SLOT(Q_, WORK_)                                                                          \
+  {                                                                                                       \
+    constexpr int s_ = (Q_) / 4, kb_ = (Q_) % 4;                                                          \
+    const v16i z = {};                                                                                    \
+    snext[kb_] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kk[(Q_) & 1], qq[s_ & 1], s_ == 0 ? z : snext[kb_], 0, \
+                                                       0, 0);                                             \
+    if ((Q_) + 2 < NQK) {                                                                                 \
+      if (((Q_) + 2) % 4 == 0) qq[(((Q_) + 2) / 4) & 1] = SAGE_QOP(((Q_) + 2) / 4);                       \
+      kk[(Q_) & 1] = SAGE_KOP((Q_) + 2);                                                                  \
+    }                                                                                                     \
+    WORK_;                                                                                                \
+    SAGE_FENCE();                                                                                         \
   }
   if constexpr (D == 128) {
-  SAGE_QK_SLOT(0, 0, 0, 1, SAGE_EXP(2, 0))
-  SAGE_QK_SLOT(0, 1, 0, 2, (void)0)
-  SAGE_QK_SLOT(0, 2, 0, 3, SAGE_EXP(2, 1))
-  SAGE_QK_SLOT(0, 3, 1, 0, (void)0)
-  SAGE_QK_SLOT(1, 0, 1, 1, SAGE_EXP(2, 2))
-  SAGE_QK_SLOT(1, 1, 1, 2, (void)0)
-  SAGE_QK_SLOT(1, 2, 1, 3, SAGE_EXP(2, 3))
-  SAGE_QK_SLOT(1, 3, 2, 0, (void)0)
-  SAGE_QK_SLOT(2, 0, 2, 1, SAGE_EXP(3, 0))
-  SAGE_QK_SLOT(2, 1, 2, 2, (void)0)
-  SAGE_QK_SLOT(2, 2, 2, 3, SAGE_EXP(3, 1))
-  SAGE_QK_SLOT(2, 3, 3, 0, (void)0)
-  SAGE_QK_SLOT(3, 0, 3, 1, SAGE_EXP(3, 2))
-  SAGE_QK_SLOT(3, 1, 3, 2, (void)0)
-  SAGE_QK_SLOT(3, 2, 3, 3, SAGE_EXP(3, 3))
-  SAGE_QK_SLOT(3, 3, -1, 0, SAGE_L_UPDATE())
+  SAGE_QK_SLOT(0, SAGE_EXP(2, 0))
+  SAGE_QK_SLOT(1, (void)0)
+  SAGE_QK_SLOT(2, SAGE_EXP(2, 1))
+  SAGE_QK_SLOT(3, (void)0)
+  SAGE_QK_SLOT(4, SAGE_EXP(2, 2))
+  SAGE_QK_SLOT(5, (void)0)
+  SAGE_QK_SLOT(6, SAGE_EXP(2, 3))
+  SAGE_QK_SLOT(7, (void)0)
+  SAGE_QK_SLOT(8, SAGE_EXP(3, 0))
+  SAGE_QK_SLOT(9, (void)0)
+  SAGE_QK_SLOT(10, SAGE_EXP(3, 1))
+  SAGE_QK_SLOT(11, (void)0)
+  SAGE_QK_SLOT(12, SAGE_EXP(3, 2))
+  SAGE_QK_SLOT(13, (void)0)
+  SAGE_QK_SLOT(14, SAGE_EXP(3, 3))
+  SAGE_QK_SLOT(15, SAGE_L_UPDATE())
   } else {
-  SAGE_QK_SLOT(0, 0, 0, 1, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
-  SAGE_QK_SLOT(0, 1, 0, 2, { SAGE_EXP(1, 2); SAGE_EXP(1, 3); })
+  SAGE_QK_SLOT(0, { SAGE_EXP(1, 0); SAGE_EXP(1, 1); })
+  SAGE_QK_SLOT(1, { SAGE_EXP(1, 2); SAGE_EXP(1, 3); })
   // pk[1] of the previous tile has been handed to its MFMAs as well
-  SAGE_QK_SLOT(0, 2, 0, 3, { SAGE_EXP(2, 0); SAGE_EXP(2, 1); })
-  SAGE_QK_SLOT(0, 3, 1, 0, { SAGE_EXP(2, 2); SAGE_EXP(2, 3); })
-  SAGE_QK_SLOT(1, 0, 1, 1, { SAGE_EXP(3, 0); SAGE_EXP(3, 1); })
-  SAGE_QK_SLOT(1, 1, 1, 2, { SAGE_EXP(3, 2); SAGE_EXP(3, 3); })
-  SAGE_QK_SLOT(1, 2, 1, 3, SAGE_L_UPDATE())
-  SAGE_QK_SLOT(1, 3, -1, 0, (void)0)
+  SAGE_QK_SLOT(2, { SAGE_EXP(2, 0); SAGE_EXP(2, 1); })
+  SAGE_QK_SLOT(3, { SAGE_EXP(2, 2); SAGE_EXP(2, 3); })
+  SAGE_QK_SLOT(4, { SAGE_EXP(3, 0); SAGE_EXP(3, 1); })
+  SAGE_QK_SLOT(5, { SAGE_EXP(3, 2); SAGE_EXP(3, 3); })
+  SAGE_QK_SLOT(6, SAGE_L_UPDATE())
+  SAGE_QK_SLOT(7, (void)0)
   }
 #undef SAGE_L_UPDATE
 #undef SAGE_QK_SLOT
+#undef SAGE_KOP
+#undef SAGE_QOP
 #undef SAGE_EXP
   // Rescale O to the new maximum (the previous tile's PV has completed by
   // now), only when some lane's maximum moved: alpha exactly 1 multiplies by
