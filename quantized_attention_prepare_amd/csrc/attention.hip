@@ -491,7 +491,10 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   for (int i = 0; i < C; ++i)
     v_lane_off[i] = (uint32_t)(lane >> 3) * spad32 + (uint32_t)(((lane & 7) ^ (((lane >> 4) & 3) | ((i & 1) << 2))) * 16);
   const float* ks = k_scale + bh * (S_pad / kQBlock);
-  const float qs = active ? q_scale[bh * (S_pad / kQBlock) + q0 / kQBlock] : 0.0f;
+  float qs = active ? q_scale[bh * (S_pad / kQBlock) + q0 / kQBlock] : 0.0f;
+  // kept in a vector register: a VALU operation reads at most one scalar
+  // register, and the key-block scales arrive in scalar registers
+  asm volatile("" : "+v"(qs));
 
   // This wave's 32 query rows go to LDS once (zeros past S_pad); the score
   // MFMAs read their B operand from there.
@@ -545,13 +548,13 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // Causal: the last visited tile holds the workgroup's own queries; there
   // the lane sees keys below min(32 wave + col + 1, nvalid), and blocks at or
   // past min(32 (wave + 1), nvalid) are masked for the whole wave.
-#define SAGE_ITERATION(T_, HAS_PREV_, CUR_, NEXT_)                                                             \
+#define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                             \
   {                                                                                                            \
     const int t_ = (T_);                                                                                       \
     __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                      \
     __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                  \
-    if (t_ + 2 < ntw) load_k<D>(KBUF(t_ & 1), rk, t_ + 2, k_lane_off, wave);                                   \
-    load_v<D>(VBUF(t_ & 1), rv, t_, spad32, v_lane_off, wave);                                                 \
+    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                     \
+    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                   \
     const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                                \
     const bool diag = kCausal && t_ == ntw - 1;                                                                \
     const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                             \
@@ -560,16 +563,18 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
     for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;               \
     if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                               \
     tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                              \
-                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((t_ + 1) & 1),         \
-                                 KBUF((t_ + 1) & 1), qrow, half, col, prow);                                   \
+                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1),           \
+                                 KBUF((PAR_) ^ 1), qrow, half, col, prow);                                     \
   }
-  SAGE_ITERATION(0, false, sa, sb)
+  // tile t uses buffer pair t & 1; the parity is spelled out so that buffer
+  // addresses fold into the LDS instructions' offsets (t is odd in the loop)
+  SAGE_ITERATION(0, 0, false, sa, sb)
   int t = 1;
   for (; t + 1 < ntw; t += 2) {
-    SAGE_ITERATION(t, true, sb, sa)
-    SAGE_ITERATION(t + 1, true, sa, sb)
+    SAGE_ITERATION(t, 1, true, sb, sa)
+    SAGE_ITERATION(t + 1, 0, true, sa, sb)
   }
-  if (t < ntw) SAGE_ITERATION(t, true, sb, sa)
+  if (t < ntw) SAGE_ITERATION(t, 1, true, sb, sa)
 #undef SAGE_ITERATION
   if constexpr (kCausal) {
     // Clear the FP8 codes of the diagonal tile's masked keys (those at or past
