@@ -309,6 +309,31 @@ def test_causal_attention_and_lse(sage, B, S, H, D, smooth_k):
     check_lse(f"causal_lse{B}x{S}x{H}x{D}", lse.cpu().numpy(), lse_o)
 
 
+@pytest.mark.parametrize("qscale", [0.0, 2.0 ** -40])
+@pytest.mark.parametrize("B,S,H,D,causal", [(1, 300, 2, 128, False), (2, 333, 2, 128, True),
+                                             (1, 1000, 2, 64, True), (1, 200, 3, 64, False)])
+def test_vanishing_score_scale_keeps_masked_keys_out(sage, qscale, B, S, H, D, causal):
+    """Q scaled to 0 or by 2^-40 makes every score (nearly) 0, and then a masked
+    key's score, however low its integer stand-in, times the block's scale is
+    no longer far below the row maximum. Only the infinite scale of blocks that
+    no lane sees, the correction of l for the partly masked block and (causal)
+    the cleared FP8 codes keep padded and masked keys out of the row. Every
+    visible key has (nearly) the same weight here, so one leaked key moves the
+    output and the log-sum-exp visibly."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=True, base_seed=6200 + S + D + int(causal))
+    q, k, v = inputs(w)
+    qt = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16) * qscale   # exact: a power of two or zero
+    q = qt.contiguous().view(torch.int16).numpy().view(np.uint16)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", causal, w.sm_scale, True, True)
+    torch.cuda.synchronize()
+    R, lse_o = oracle.attn(oracle.prepare(q, k, v, True), w.sm_scale, want_lse=True, causal=causal)
+    E = oracle.exact(q, k, v, w.sm_scale, causal=causal)
+    name = f"qscale{qscale:g}_{B}x{S}x{H}x{D}{'_causal' if causal else ''}"
+    compare_attention(name, out.view(torch.int16).cpu().numpy().view(np.uint16), R, E)
+    check_lse("lse_" + name, lse.cpu().numpy(), lse_o)
+
+
 def test_causal_last_row_is_the_non_causal_row(sage):
     """The last query sees every key, and on the diagonal tile the cleared
     codes of the padded keys multiplied V codes that are zero anyway: the
