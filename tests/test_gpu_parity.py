@@ -309,17 +309,19 @@ def test_causal_attention_and_lse(sage, B, S, H, D, smooth_k):
     check_lse(f"causal_lse{B}x{S}x{H}x{D}", lse.cpu().numpy(), lse_o)
 
 
-@pytest.mark.parametrize("qscale", [0.0, 2.0 ** -40])
+@pytest.mark.parametrize("qscale", [0.0, 2.0 ** -40, 2.0 ** 8])
 @pytest.mark.parametrize("B,S,H,D,causal", [(1, 300, 2, 128, False), (2, 333, 2, 128, True),
                                              (1, 1000, 2, 64, True), (1, 200, 3, 64, False)])
-def test_vanishing_score_scale_keeps_masked_keys_out(sage, qscale, B, S, H, D, causal):
+def test_extreme_score_scales_keep_masked_keys_out(sage, qscale, B, S, H, D, causal):
     """Q scaled to 0 or by 2^-40 makes every score (nearly) 0, and then a masked
     key's score, however low its integer stand-in, times the block's scale is
     no longer far below the row maximum. Only the infinite scale of blocks that
     no lane sees, the correction of l for the partly masked block and (causal)
     the cleared FP8 codes keep padded and masked keys out of the row. Every
-    visible key has (nearly) the same weight here, so one leaked key moves the
-    output and the log-sum-exp visibly."""
+    visible key has (nearly) the same weight there, so one leaked key moves the
+    output and the log-sum-exp visibly. Q scaled by 2^8 is the other end:
+    scores of hundreds (log2 units), rows close to one-hot, the running maximum
+    jumping by more than the exponent range so that alpha underflows to 0."""
     import torch
     w = synth.custom(B, S, H, D=D, smooth_k=True, base_seed=6200 + S + D + int(causal))
     q, k, v = inputs(w)
