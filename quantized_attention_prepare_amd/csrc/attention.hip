@@ -548,23 +548,23 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // Causal: the last visited tile holds the workgroup's own queries; there
   // the lane sees keys below min(32 wave + col + 1, nvalid), and blocks at or
   // past min(32 (wave + 1), nvalid) are masked for the whole wave.
-#define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                             \
-  {                                                                                                            \
-    const int t_ = (T_);                                                                                       \
-    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                      \
-    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                  \
-    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                     \
-    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                   \
-    const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                                \
-    const bool diag = kCausal && t_ == ntw - 1;                                                                \
-    const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                             \
-    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                         \
-    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */   \
-    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;               \
-    if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                               \
-    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                              \
-                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1),           \
-                                 KBUF((PAR_) ^ 1), qrow, half, col, prow);                                     \
+#define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                     \
+  {                                                                                                          \
+    const int t_ = (T_);                                                                                     \
+    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                    \
+    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                \
+    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                   \
+    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                 \
+    const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                              \
+    const bool diag = kCausal && t_ == ntw - 1;                                                              \
+    const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                           \
+    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                       \
+    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */ \
+    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;             \
+    if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                             \
+    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                            \
+                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1),         \
+                                 KBUF((PAR_) ^ 1), qrow, half, col, prow);                                   \
   }
   // tile t uses buffer pair t & 1; the parity is spelled out so that buffer
   // addresses fold into the LDS instructions' offsets (t is odd in the loop)
