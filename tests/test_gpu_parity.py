@@ -448,6 +448,41 @@ def test_tensors_past_2_31_elements(sage):
     torch.cuda.empty_cache()
 
 
+def test_tensors_past_2_31_elements_hnd(sage):
+    """The same size in the HND layout ([B, H, S, D] inputs, output written
+    through an HND view): here the head stride S*D carries the offsets past
+    2^31 (the last head starts at element 2.4e9), in the prologue's loads and
+    in the attention epilogue's stores."""
+    import torch
+    B, S, H, D = 3, 65536, 96, 128
+    gen = torch.Generator(device="cuda").manual_seed(7100)
+    q = torch.randn((B, H, S, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((B, H, S, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k.add_(0.5)
+    v = torch.randn((B, H, S, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+    assert q[B - 1, H - 1].storage_offset() > 2 ** 31
+    sm = 1.0 / math.sqrt(D)
+    prep = sage.prepare(q, k, v, True, layout="HND")
+    out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    sage.attn(prep, sm, out=out.permute(0, 2, 1, 3))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 127, 128, 40000, S - 129, S - 2, S - 1], dtype=np.int64)
+    for b, h in ((0, 0), (1, 47), (B - 1, H - 1)):
+        host = [x[b, h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for x in (q, k, v)]
+        o = oracle.prepare_head(*host, True)
+        g = {key: prep[key][b, h].cpu().numpy() for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale",
+                                                            "k_mean")}
+        check_prologue({key: val[None, None] for key, val in g.items()},
+                       {key: val[None, None] for key, val in o.items()}, S)
+        if (b, h) == (B - 1, H - 1):
+            R = oracle.attn_rows_head(o, rows, sm)
+            E = oracle.exact_rows_head(*host, rows, sm)
+            G = out[b, h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+            compare_attention("past_2^31_last_head_hnd", G, R, E)
+    del q, k, v, prep, out
+    torch.cuda.empty_cache()
+
+
 def test_fused_calls_replay_from_a_hip_graph(sage):
     """sageattn, causal and not, captured in one HIP graph (the library launches
     kernels only: no allocation, memset or synchronisation inside) and replayed
