@@ -379,7 +379,11 @@ def test_causal_workload_rows(sage, name, n):
 
 
 # ------------------------------------------------------------------ randomized sweep
-def _random_cases(n=24, seed=20261202):
+def _random_cases(n=None, seed=None):
+    # 24 cases from a fixed seed by default; SAGE_RANDOM_CASES and SAGE_RANDOM_SEED
+    # run a longer or different sweep
+    n = int(os.environ.get("SAGE_RANDOM_CASES", "24")) if n is None else n
+    seed = int(os.environ.get("SAGE_RANDOM_SEED", "20261202")) if seed is None else seed
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
