@@ -417,6 +417,49 @@ def test_random_configurations_against_the_oracle(sage, i, B, S, H, D, smooth_k,
     check_lse(f"random{i}_lse", lse.cpu().numpy(), lse_o)
 
 
+def _larger_cases(n=6, seed=4242):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B, H, S = int(rng.integers(1, 3)), int(rng.integers(1, 7)), int(rng.integers(2000, 20000))
+        cases.append((i, B, S, H, int(rng.choice([64, 128])), bool(rng.integers(0, 2)), bool(rng.integers(0, 2)),
+                      str(rng.choice(["NHD", "HND"]))))
+    return cases
+
+
+@pytest.mark.parametrize("i,B,S,H,D,smooth_k,causal,layout", _larger_cases())
+def test_random_larger_configurations_on_sampled_rows(sage, i, B, S, H, D, smooth_k, causal, layout):
+    """Seeded random shapes with S between 2 000 and 20 000 (many key tiles, a
+    ragged last one): output and log-sum-exp on about 200 sampled rows plus the
+    rows at the first and last tile edges of the last head, the last head's
+    prologue bit for bit."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=9000 + i)
+    q, k, v = inputs(w)
+    tq, tk, tv = (to_dev(x) for x in (q, k, v))
+    if layout == "HND":
+        tq, tk, tv = (x.permute(0, 2, 1, 3).contiguous() for x in (tq, tk, tv))
+    out, lse = sage.sageattn(tq, tk, tv, layout, causal, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    if layout == "HND":
+        out = out.permute(0, 2, 1, 3).contiguous()
+    edge = np.array([[B - 1, H - 1, s] for s in (0, 127, 128, S - 129, S - 128, S - 1)], dtype=np.int64)
+    rows = np.unique(np.concatenate([synth.sample_rows(w, 192), edge]), axis=0)
+    heads = sorted({(int(b), int(h)) for b, h, _ in rows})
+    prep = oracle.prepare(q, k, v, smooth_k, heads=heads)
+    R, lse_o = oracle.attn(prep, w.sm_scale, rows=rows, want_lse=True, causal=causal)
+    E = oracle.exact(q, k, v, w.sm_scale, rows=rows, causal=causal)
+    O = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    name = f"larger{i}_{B}x{S}x{H}x{D}_{'sk' if smooth_k else 'nosk'}_{'c' if causal else 'nc'}_{layout}"
+    compare_attention(name, O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E)
+    check_lse(name + "_lse", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
+    g = gpu_prepare(sage, q, k, v, smooth_k)
+    b, h = B - 1, H - 1
+    o = oracle.prepare_head(q[b, :, h].copy(), k[b, :, h].copy(), v[b, :, h].copy(), smooth_k)
+    check_prologue({key: val[b:b + 1, h:h + 1] for key, val in g.items()}, {key: val[None, None] for key, val in o.items()},
+                   S)
+
+
 # ------------------------------------------------------------------ 64-bit offsets, graph capture
 def test_tensors_past_2_31_elements(sage):
     """B*S*H*D = 3*65536*96*128 > 2^31 elements (4.8 GB per BF16 tensor): the
