@@ -284,10 +284,6 @@ def main():
     pro_bytes = prologue_compulsory_bytes(w)
     pro_traffic = load_prologue_traffic(w.name)
     cold = cold_prologue(w)
-    cold["gbs"] = round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1)
-    # the counters' bytes are what the L2 fetches and writes; warm calls find part of
-    # them in the memory-side cache, flushed ones mostly in HBM
-    cold["achieved_gbs"] = round(pro_traffic / (cold["median_ms"] * 1e-3) / 1e9, 1) if pro_traffic else None
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         base, _, mode = name.partition(":")
@@ -335,15 +331,23 @@ def main():
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "attn_kernel", "kernel_ms": round(r["attn_ms"], 4),
                      "algorithmic_per_launch": f"{fl:.4e} ops (4*D ops per query-key pair)"},
-        "prologue": {"ms": round(r["prologue_ms"], 4), "compulsory_bytes": pro_bytes,
-                     "gbs": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        # the prologue's headline is a call with the memory-side cache flushed first (as in
+        # the step, where each prologue follows an attention launch's traffic); back-to-back
+        # calls on the same inputs find part of them in that cache ("warm")
+        "prologue": {"ms": cold["median_ms"], "min_ms": cold["min_ms"], "calls": cold["calls"],
+                     "cache": "flushed before each call (512 MiB written)",
+                     "compulsory_bytes": pro_bytes,
+                     "gbs": round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": pro_traffic,
-                     "achieved_gbs": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9, 1)
+                     "achieved_gbs": (round(pro_traffic / (cold["median_ms"] * 1e-3) / 1e9, 1)
                                       if pro_traffic else None),
-                     "achieved_frac_of_hbm_peak": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                     "achieved_frac_of_hbm_peak": (round(pro_traffic / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                                                    if pro_traffic else None),
-                     "cold": cold},
+                     "warm": {"ms": round(r["prologue_ms"], 4),
+                              "gbs": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9, 1),
+                              "achieved_gbs": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9, 1)
+                                               if pro_traffic else None)}},
         "step_wall_ms": round(r["step_wall_ms"], 4),
         "one_call_at_a_time": one_call_at_a_time(w, 10),
         "other_workloads": others,
