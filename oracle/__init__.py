@@ -61,6 +61,8 @@ def lib():
         L.oracle_e4m3_decode.restype = ctypes.c_float
         L.oracle_quant_block_int8.argtypes = [_P, _I, _I, _P]
         L.oracle_quant_block_int8.restype = ctypes.c_float
+        L.oracle_bf16_exact_sum.argtypes = [_P, _I, _I]
+        L.oracle_bf16_exact_sum.restype = ctypes.c_double
         L.oracle_prepare_head.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P, _P, _P]
         L.oracle_prepare_head.restype = ctypes.c_int
         L.oracle_attn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, ctypes.c_float, _I, ctypes.c_int, _P, _I,
@@ -110,6 +112,12 @@ def quant_block_int8(x: np.ndarray) -> tuple[np.ndarray, float]:
     q = np.empty((rows, D), dtype=np.int8)
     s = lib().oracle_quant_block_int8(_ptr(x), rows, D, _ptr(q))
     return q, float(s)
+
+
+def bf16_exact_sum(x: np.ndarray) -> float:
+    """Exact sum of BF16 values (uint16 bits) rounded once to double."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.uint16).ravel())
+    return float(lib().oracle_bf16_exact_sum(_ptr(x), x.size, 1))
 
 
 # ------------------------------------------------------------ prologue

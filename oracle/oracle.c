@@ -82,7 +82,19 @@ uint8_t oracle_e4m3_encode(float x) {
  * block is 32 consecutive tokens of one head times all D channels (a tail
  * block holds the remaining rows); symmetric absmax scaling onto [-127, 127]
  * with scale = a/127; codes are rint(x * (127/a)) (round half to even), so the
- * division happens once per block. */
+ * division happens once per block.
+ * Blocks of tiny values: for a below 2^-64 the quotient 127/a can exceed the
+ * largest float (it does below about 3.7e-37, which finite BF16 inputs and
+ * mean-subtracted keys reach), so such a block is first multiplied by 2^64,
+ * exactly for every element, and a with it; the codes are then formed as
+ * above from the scaled values. Wherever 127/a is a finite float the codes are
+ * the same as without the step: the scaled quotient is exactly 2^-64 times the
+ * unscaled one and the scaled element exactly 2^64 times the unscaled one, so
+ * every product rounds the same real number. The scale stays a/127 of the
+ * unscaled a (it may be subnormal, or 0 below about 127 * 2^-150). */
+#define ORACLE_TINY 0x1p-64f
+#define ORACLE_TINY_LIFT 0x1p64f
+
 float oracle_quant_block_int8(const float* x, int64_t rows, int64_t D, int8_t* q) {
   float a = 0.0f;
   for (int64_t i = 0; i < rows * D; ++i) {
@@ -94,15 +106,84 @@ float oracle_quant_block_int8(const float* x, int64_t rows, int64_t D, int8_t* q
     return 0.0f;
   }
   float scale = a / 127.0f;
-  float inv = 127.0f / a;
+  float lift = a < ORACLE_TINY ? ORACLE_TINY_LIFT : 1.0f;
+  float inv = 127.0f / (a * lift);
   for (int64_t i = 0; i < rows * D; ++i) {
-    float y = x[i] * inv;
+    float y = (x[i] * lift) * inv;
     float r = rintf(y);
     if (r > 127.0f) r = 127.0f;
-    if (r < -127.0f) r = -127.0f;
+    /* for finite inputs r is finite; the comparison is written so that a NaN
+     * (possible only from non-finite inputs, outside the method's domain)
+     * still gives a defined integer conversion */
+    if (!(r >= -127.0f)) r = -127.0f;
     q[i] = (int8_t)r;
   }
   return scale;
+}
+
+/* ---------------------------------------------------------- fp64 sum --- */
+/* Release notes, "What changed": with smooth_k on, the key mean is summed in
+ * fp64. Reading: the fp64 sum of a channel is its exact sum rounded once to
+ * double (nearest, ties to even), the most accurate fp64 sum and the same in
+ * whatever order the terms are taken.
+ * A finite BF16 value is M * 2^(e - 133) with an integer 0 <= M < 256 and
+ * 0 <= e <= 253 (exponent field E > 0: M = 128 + mantissa, e = E - 1; E = 0:
+ * M = mantissa, e = 0), so the exact sum of n < 2^25 of them is an integer
+ * multiple of 2^-133 below 2^286 in magnitude. It is accumulated here as two
+ * non-negative integers (positive and negative terms) of ten 32-bit limbs,
+ * then rounded. Returns NaN if a value is not finite. */
+#define ORACLE_LIMBS 10
+
+static void big_add_shifted(uint32_t* acc, uint32_t M, int e) {
+  uint64_t carry = (uint64_t)M << (e % 32);   /* < 2^39, spans limbs e/32 and e/32 + 1 */
+  for (int j = e / 32; j < ORACLE_LIMBS && carry != 0; ++j) {
+    uint64_t t = (uint64_t)acc[j] + (carry & 0xFFFFFFFFu);
+    acc[j] = (uint32_t)t;
+    carry = (carry >> 32) + (t >> 32);
+  }
+}
+
+static int big_bit(const uint32_t* x, int bit) { return (int)((x[bit / 32] >> (bit % 32)) & 1u); }
+
+double oracle_bf16_exact_sum(const uint16_t* x, int64_t n, int64_t stride) {
+  uint32_t pos[ORACLE_LIMBS] = {0}, neg[ORACLE_LIMBS] = {0};
+  for (int64_t i = 0; i < n; ++i) {
+    uint16_t b = x[i * stride];
+    uint32_t E = (b >> 7) & 0xFFu, man = b & 0x7Fu;
+    if (E == 0xFFu) return NAN;
+    uint32_t M = E ? 128u + man : man;
+    int e = E ? (int)E - 1 : 0;
+    big_add_shifted((b >> 15) ? neg : pos, M, e);
+  }
+  /* magnitude = |pos - neg|, by limbs from the most significant */
+  int negative = 0;
+  for (int j = ORACLE_LIMBS - 1; j >= 0; --j)
+    if (pos[j] != neg[j]) { negative = neg[j] > pos[j]; break; }
+  const uint32_t* big = negative ? neg : pos;
+  const uint32_t* small = negative ? pos : neg;
+  uint32_t mag[ORACLE_LIMBS];
+  int64_t borrow = 0;
+  for (int j = 0; j < ORACLE_LIMBS; ++j) {
+    int64_t t = (int64_t)big[j] - (int64_t)small[j] - borrow;
+    borrow = t < 0;
+    mag[j] = (uint32_t)(t + (borrow ? ((int64_t)1 << 32) : 0));
+  }
+  /* most significant set bit */
+  int p = 32 * ORACLE_LIMBS - 1;
+  while (p >= 0 && !big_bit(mag, p)) --p;
+  if (p < 0) return 0.0;
+  /* the top 64 bits (or all of them), with every lower bit ORed into bit 0:
+   * bit 0 lies below the rounding position of a 53-bit significand, so the
+   * one rounding of the uint64 -> double conversion is the rounding of the
+   * whole magnitude */
+  uint64_t u = 0;
+  int low = p >= 63 ? p - 63 : 0;
+  for (int bit = p; bit >= low; --bit) u = (u << 1) | (uint64_t)big_bit(mag, bit);
+  int sticky = 0;
+  for (int bit = low - 1; bit >= 0; --bit) sticky |= big_bit(mag, bit);
+  u |= (uint64_t)sticky;
+  double d = ldexp((double)u, low - 133);
+  return negative ? -d : d;
 }
 
 /* ----------------------------------------------------------- prologue --- */
@@ -115,17 +196,13 @@ int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (!rowsbuf) return -1;
 
   /* Release notes, "What changed": with smooth_k on, the key mean is summed
-   * in fp64. Reading: per channel d, the sum over all S tokens in ascending
-   * order in double, divided by S in double, rounded once to float; it is
-   * then subtracted from every key in float. With smooth_k off nothing is
-   * subtracted and k_mean is zero. */
+   * in fp64. Reading: per channel d, the exact sum over all S tokens rounded
+   * once to double (oracle_bf16_exact_sum), divided by S in double, rounded
+   * once to float; it is then subtracted from every key in float. With
+   * smooth_k off nothing is subtracted and k_mean is zero. */
   for (int64_t d = 0; d < D; ++d) {
     float km = 0.0f;
-    if (smooth_k && S > 0) {
-      double sum = 0.0;
-      for (int64_t s = 0; s < S; ++s) sum += (double)oracle_bf16_decode(k[s * row_stride + d]);
-      km = (float)(sum / (double)S);
-    }
+    if (smooth_k && S > 0) km = (float)(oracle_bf16_exact_sum(k + d, S, row_stride) / (double)S);
     k_mean[d] = km;
   }
 
@@ -160,8 +237,13 @@ int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       continue;
     }
     v_scale[d] = a / 448.0f;
-    float inv = 448.0f / a;
-    for (int64_t s = 0; s < S; ++s) dst[s] = oracle_e4m3_encode(oracle_bf16_decode(v[s * row_stride + d]) * inv);
+    /* a channel of tiny values is lifted by 2^64 first, as an INT8 block is
+     * (448/a overflows below about 1.3e-36); the codes are unchanged wherever
+     * 448/a is a finite float */
+    float lift = a < ORACLE_TINY ? ORACLE_TINY_LIFT : 1.0f;
+    float inv = 448.0f / (a * lift);
+    for (int64_t s = 0; s < S; ++s)
+      dst[s] = oracle_e4m3_encode((oracle_bf16_decode(v[s * row_stride + d]) * lift) * inv);
     for (int64_t s = S; s < S_pad; ++s) dst[s] = 0;
   }
   free(rowsbuf);

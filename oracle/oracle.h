@@ -12,7 +12,7 @@
  *     FP32 accumulation; Q and K are quantized per 32-row block and V per
  *     channel.
  *   - release notes, "What changed", fourth item: with smooth_k on, the key
- *     mean is summed in fp64.
+ *     mean is summed in fp64 (read as the exact sum rounded once to double).
  *   - issue, "What I have so far": the accepted problem is BF16 [B,S,H,128],
  *     equal Q/K/V shapes, no mask, non-causal.
  * Steps the pages leave open (absmax scaling, e4m3 for V, the exp2 online
@@ -44,8 +44,15 @@ float oracle_e4m3_decode(uint8_t c);
 /* INT8 quantization of one 32-row block (rows x D floats, rows <= 32):
  * a = max|x|; scale = a/127; q = rint(x * (127/a)) clamped to [-127,127]
  * (each a single correctly rounded float operation; ties to even).
+ * A block with a < 2^-64 is multiplied by 2^64 first (x and a), which keeps
+ * 127/a finite and changes no code wherever it was finite already.
  * An all-zero block gets scale 0 and all-zero codes. Returns the scale. */
 float oracle_quant_block_int8(const float* x, int64_t rows, int64_t D, int8_t* q);
+
+/* Exact sum of n BF16 values x[0], x[stride], ... rounded once to double
+ * (nearest, ties to even): the reading of "summed in fp64". NaN if a value
+ * is not finite. */
+double oracle_bf16_exact_sum(const uint16_t* x, int64_t n, int64_t stride);
 
 /* The prologue for one head. q, k, v point at row s=0 of the head in a BF16
  * tensor whose consecutive rows (tokens) are row_stride elements apart (H*D
@@ -53,9 +60,15 @@ float oracle_quant_block_int8(const float* x, int64_t rows, int64_t D, int8_t* q
  * Outputs (nb = ceil(S/32), S_pad >= S):
  *   q8[S][D], q_scale[nb], k8[S][D], k_scale[nb]   INT8 per 32-row block
  *   v8t[D][S_pad], v_scale[D]                      e4m3 per channel, transposed,
- *                                                  columns S..S_pad-1 zero
- *   k_mean[D]                                      smooth_k: fp32 of the fp64
- *                                                  mean over S; else zeros
+ *                                                  columns S..S_pad-1 zero (a
+ *                                                  channel with absmax < 2^-64
+ *                                                  is lifted by 2^64 first, as
+ *                                                  an INT8 block is)
+ *   k_mean[D]                                      smooth_k: float of (the exact
+ *                                                  sum rounded to double) / S;
+ *                                                  else zeros
+ * Inputs must be finite, and with smooth_k every K - k_mean must be a finite
+ * float (true whenever |K| <= 2^126); other inputs give unspecified codes.
  * Returns 0, or -1 for S < 0 or D < 1. */
 int oracle_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S, int64_t D,
                         int64_t row_stride, int smooth_k, int64_t S_pad, int8_t* q8, float* q_scale, int8_t* k8,

@@ -26,7 +26,11 @@ static uint16_t bf16_of(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-static int run(int64_t S, int64_t D, int smooth_k) {
+/* tiny = 1: Q, K and V values of order 1e-39 (BF16 subnormals, blocks and
+ * channels whose absmax makes 127/a and 448/a overflow a float);
+ * tiny = 2: K channels mixing magnitudes 2^60 and 2^-60 (an fp64 running sum
+ * of them is not exact). */
+static int run(int64_t S, int64_t D, int smooth_k, int tiny) {
   const int64_t S_pad = (S + 127) / 128 * 128, nb = (S + 31) / 32;
   uint16_t* q = malloc((size_t)(S * D) * 2);
   uint16_t* k = malloc((size_t)(S * D) * 2);
@@ -38,10 +42,12 @@ static int run(int64_t S, int64_t D, int smooth_k) {
   float* ks = malloc((size_t)nb * 4);
   float* vs = malloc((size_t)D * 4);
   float* km = malloc((size_t)D * 4);
+  const float f = tiny == 1 ? 1e-39f : 1.0f;
   for (int64_t i = 0; i < S * D; ++i) {
-    q[i] = bf16_of((float)(4.0 * next_uniform() - 2.0));
-    k[i] = bf16_of((float)(3.0 * next_uniform() - 1.0));
-    v[i] = bf16_of((float)(2.0 * next_uniform() - 1.0));
+    q[i] = bf16_of((float)(4.0 * next_uniform() - 2.0) * f);
+    k[i] = bf16_of((float)(3.0 * next_uniform() - 1.0) * f);
+    v[i] = bf16_of((float)(2.0 * next_uniform() - 1.0) * f);
+    if (tiny == 2) k[i] = bf16_of((float)(next_uniform() - 0.5) * ((i / D) % 2 ? 0x1p60f : 0x1p-60f));
   }
   int bad = oracle_prepare_head(q, k, v, S, D, D, smooth_k, S_pad, q8, qs, k8, ks, v8t, vs, km) != 0;
   int64_t rows[6] = {0, S / 3, S / 2, S - 1, S > 1 ? 1 : 0, S > 129 ? 128 : 0};
@@ -55,7 +61,9 @@ static int run(int64_t S, int64_t D, int smooth_k) {
     bad |= oracle_attn_rows(q8, qs, k8, ks, v8t, S_pad, vs, S, D, 0.088f, 16, causal, rows, 6, NULL, ob, NULL) != 0;
     bad |= oracle_exact_rows(q, k, v, S, D, D, 0.088, causal, rows, 6, oe, lse_e) != 0;
     for (int i = 0; i < 6 * (int)D; ++i) bad |= !isfinite(of[i]) || !isfinite(oe[i]);
-    for (int i = 0; i < 6; ++i) bad |= !isfinite(lse[i]) || !isfinite(lse_e[i]);
+    /* the log-sum-exp of scores that all vanish is still finite; exact
+     * attention's may underflow to ln 0 only in the tiny case */
+    for (int i = 0; i < 6; ++i) bad |= !isfinite(lse[i]) || (!tiny && !isfinite(lse_e[i]));
   }
   free(q); free(k); free(v); free(q8); free(k8); free(v8t); free(qs); free(ks); free(vs); free(km);
   free(of); free(ob); free(lse); free(oe); free(lse_e);
@@ -67,11 +75,19 @@ int main(void) {
   int bad = 0;
   for (size_t i = 0; i < sizeof lengths / sizeof lengths[0]; ++i)
     for (int64_t D = 64; D <= 128; D += 64)
-      for (int smooth = 0; smooth < 2; ++smooth) {
-        int r = run(lengths[i], D, smooth);
-        if (r) fprintf(stderr, "failed: S=%lld D=%lld smooth_k=%d\n", (long long)lengths[i], (long long)D, smooth);
-        bad |= r;
-      }
+      for (int smooth = 0; smooth < 2; ++smooth)
+        for (int tiny = 0; tiny < 3; ++tiny) {
+          int r = run(lengths[i], D, smooth, tiny);
+          if (r)
+            fprintf(stderr, "failed: S=%lld D=%lld smooth_k=%d tiny=%d\n", (long long)lengths[i], (long long)D,
+                    smooth, tiny);
+          bad |= r;
+        }
+  /* the exact sum of a channel: 2^60, 1, -2^60 in that order sums to 1 */
+  {
+    const uint16_t x[3] = {bf16_of(0x1p60f), bf16_of(1.0f), bf16_of(-0x1p60f)};
+    bad |= oracle_bf16_exact_sum(x, 3, 1) != 1.0;
+  }
   /* argument checks: rows out of range, bad sizes */
   int64_t row = 5;
   bad |= oracle_attn_rows(NULL, NULL, NULL, NULL, NULL, 128, NULL, 4, 128, 0.1f, 128, 0, &row, 1, NULL, NULL, NULL) != -1;

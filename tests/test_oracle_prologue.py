@@ -193,3 +193,127 @@ def test_full_tensor_prepare_matches_per_head():
             one = oracle.prepare_head(q[b, :, h], k[b, :, h], v[b, :, h], True)
             for key in one:
                 assert np.array_equal(full[key][b, h], one[key]), key
+
+
+# ------------------------------------------------------------ blocks and channels of tiny values
+def test_int8_tiny_block_hand_worked():
+    # a = 2^-130 (a BF16 subnormal): 127/a overflows a float, so the block is
+    # lifted by 2^64 first.  Worked by hand from x * 127 / a:
+    #   2^-130     -> 127
+    #   -2^-131    -> -63.5  -> -64 (tie to even)
+    #   3 * 2^-133 -> 47.625 -> 48
+    #   2^-132     -> 31.75  -> 32
+    #   0          -> 0
+    x = np.zeros((32, 128), np.float32)
+    x[0, 0], x[0, 1], x[5, 7], x[31, 127] = 2.0 ** -130, -(2.0 ** -131), 3 * 2.0 ** -133, 2.0 ** -132
+    assert np.array_equal(synth.bf16_to_float(bf16(x)), x)          # all BF16-exact
+    q, s = oracle.quant_block_int8(x)
+    assert (q[0, 0], q[0, 1], q[5, 7], q[31, 127]) == (127, -64, 48, 32)
+    assert np.count_nonzero(q) == 4
+    assert s == np.float32(2.0 ** -130) / np.float32(127.0)
+
+
+@pytest.mark.parametrize("exp", [-149, -140, -133, -126, -100, -70])
+def test_int8_tiny_block_codes_are_scale_invariant(exp):
+    # integer-valued blocks times 2^exp are exact floats down to the smallest
+    # subnormal; a power-of-two scale cannot change the codes, and at 2^0 the
+    # quotient 127/a is an ordinary float
+    rng = np.random.default_rng(100 - exp)
+    for rows in (32, 7):
+        xi = rng.integers(-255, 256, size=(rows, 128)).astype(np.float32)
+        xi[rng.random(xi.shape) < 0.3] = 0
+        ref, _ = oracle.quant_block_int8(xi)
+        tiny = (xi * np.float32(2.0 ** exp)).astype(np.float32)
+        assert np.array_equal(tiny.astype(np.float64) * 2.0 ** -exp, xi)   # exact
+        q, s = oracle.quant_block_int8(tiny)
+        assert np.array_equal(q, ref)
+        assert s == np.float32(np.abs(tiny).max()) / np.float32(127.0)
+
+
+def test_v_tiny_channel_codes_and_output_are_finite_and_scale_invariant():
+    S = 200
+    q, k, v = _head_inputs(S, 77)
+    vf = synth.bf16_to_float(v).copy()
+    # channel 5: absmax about 5e-37 (448/a overflows a float), its small values
+    # BF16 subnormals; channel 9: lifted, though 448/a would be finite
+    vf[:, 5] = synth.bf16_to_float(bf16(vf[:, 5] * np.float32(2.0 ** -122)))
+    vf[:, 9] = vf[:, 9] * np.float32(2.0 ** -60)
+    vt = bf16(vf)
+    assert np.array_equal(synth.bf16_to_float(vt), vf)
+    assert np.abs(vf[:, 5]).max() < 448.0 / np.finfo(np.float32).max
+    # the same channels scaled back up by exact powers of two: ordinary inputs
+    vr = vf.copy()
+    vr[:, 5] *= np.float32(2.0 ** 122)
+    vr[:, 9] *= np.float32(2.0 ** 60)
+    v = bf16(vr)
+    assert np.array_equal(synth.bf16_to_float(v), vr)
+    out = oracle.prepare_head(q, k, vt, smooth_k=False)
+    ref = oracle.prepare_head(q, k, v, smooth_k=False)
+    for d in (5, 9):
+        a = np.float32(np.abs(vf[:, d]).max())
+        assert out["v_scale"][d] == a / np.float32(448.0)
+        assert np.array_equal(out["v8t"][d], ref["v8t"][d])         # codes unchanged by the 2^-k factor
+    assert np.all((out["v8t"] & 0x7F) != 0x7F)                       # no NaN codes
+    o = oracle.bf16_bits_to_f64(oracle.attn_rows_head(out, np.arange(S), 1 / np.sqrt(128)))
+    o_ref = oracle.bf16_bits_to_f64(oracle.attn_rows_head(ref, np.arange(S), 1 / np.sqrt(128)))
+    assert np.all(np.isfinite(o))
+    # channel 9 stays a normal float: exactly the scaled output; channel 5's
+    # output lies among BF16 subnormals (spacing 2^-133), so up to that spacing
+    assert np.array_equal(o[:, 9], o_ref[:, 9] * 2.0 ** -60)
+    assert np.max(np.abs(o[:, 5] - o_ref[:, 5] * 2.0 ** -122)) <= 2.0 ** -133 * (1 + 1e-6)
+
+
+# ------------------------------------------------------------ the exact fp64 key sum
+def _bf16_exactly(vals):
+    vals = np.asarray(vals, np.float64)
+    bits = bf16(vals.astype(np.float32))
+    assert np.array_equal(synth.bf16_to_float(bits).astype(np.float64), vals)
+    return bits
+
+
+def test_exact_sum_on_adversarial_channels_matches_fsum():
+    rng = np.random.default_rng(2026)
+    chans = [
+        [2.0 ** 60, 1.0, -(2.0 ** 60), 1.0] * 50,               # ascending fp64 sum gives 1, exact 100
+        [2.0 ** 100, 2.0 ** -100, -(2.0 ** 100), 3 * 2.0 ** -98],
+        [2.0 ** 53, 1.0],                                       # tie: rounds to even (2^53)
+        [2.0 ** 53, 1.0, 2.0 ** -100],                          # just above the tie: 2^53 + 2
+        [2.0 ** 127, -(2.0 ** 127), 2.0 ** -133],               # largest and smallest magnitudes
+        [2.0 ** -133] * 7 + [-(2.0 ** -131)],                   # subnormals cancelling to 3 * 2^-133
+        [1.5, -1.5, 0.0, -0.0],                                 # exact zero
+    ]
+    for _ in range(40):                                         # random signs and exponents over the whole range
+        n = int(rng.integers(1, 3000))
+        # normal BF16 values m * 2^e (8-bit significand m) and some subnormals m * 2^-133
+        m = rng.integers(128, 256, n).astype(np.float64)
+        e = rng.integers(-133, 121, n).astype(np.float64)
+        sub = rng.random(n) < 0.1
+        m[sub], e[sub] = rng.integers(1, 128, int(sub.sum())), -133
+        sign = np.where(rng.random(n) < 0.5, -1.0, 1.0)
+        chans.append(list(sign * m * 2.0 ** e))
+    for vals in chans:
+        bits = _bf16_exactly(vals)
+        exact = math.fsum(vals)                                 # correctly rounded sum
+        assert oracle.bf16_exact_sum(bits) == exact, vals[:4]
+    # the ascending-order fp64 sum differs on the first channel, so the pin discriminates
+    acc = 0.0
+    for x in chans[0]:
+        acc += x
+    assert acc != math.fsum(chans[0])
+
+
+def test_k_mean_of_adversarial_channels_is_the_rounded_exact_mean():
+    S = 96
+    rng = np.random.default_rng(5)
+    kf = rng.standard_normal((S, 128)).astype(np.float32)
+    kf[:, 0] = np.tile(np.array([2.0 ** 60, 1.0, -(2.0 ** 60)], np.float32), S // 3)
+    kf[:, 1] = np.where(np.arange(S) % 2 == 0, np.float32(2.0 ** 70), np.float32(2.0 ** -70)) * \
+        np.where(np.arange(S) % 4 < 2, 1, -1).astype(np.float32)
+    kf[:, 2] = np.float32(2.0 ** -130) * (np.arange(S) % 5 - 2)
+    k = bf16(kf)
+    q, _, v = _head_inputs(S, 6)
+    out = oracle.prepare_head(q, k, v, smooth_k=True)
+    kd = synth.bf16_to_float(k).astype(np.float64)
+    for d in range(128):
+        assert out["k_mean"][d] == np.float32(math.fsum(kd[:, d].tolist()) / S), d
+    assert out["k_mean"][0] == np.float32(32.0 / S)

@@ -1,8 +1,10 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
- - the CPU oracle (gcc), driven through every entry point on ragged lengths,
-   both head dims, smooth_k, causal and the log-sum-exp
-   (tests/sanitize/oracle_driver.c);
+ - the CPU oracle (gcc, with float-to-integer conversion overflow checks as
+   well), driven through every entry point on ragged lengths, both head dims,
+   smooth_k, causal and the log-sum-exp, on ordinary inputs, on BF16
+   subnormals (blocks and channels whose 127/a and 448/a overflow a float)
+   and on key channels mixing 2^60 and 2^-60 (tests/sanitize/oracle_driver.c);
  - the library's C ABI with its host code instrumented (hipcc; the device code
    is built as usual), driven with 20 000 seeded random descriptors and the
    documented error cases without a GPU (tests/sanitize/abi_driver.cpp).
@@ -19,7 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
 def test_oracle_under_address_and_undefined_behaviour_sanitizers(tmp_path):
     exe = tmp_path / "oracle_driver"
-    cmd = ["gcc", "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fsanitize=address,undefined",
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fsanitize=address,undefined,float-cast-overflow",
            "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "oracle"),
            os.path.join(ROOT, "oracle", "oracle.c"), os.path.join(ROOT, "tests", "sanitize", "oracle_driver.c"),
            "-lm", "-o", str(exe)]
