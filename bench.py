@@ -212,6 +212,21 @@ def in_step_prologue(w, steps: int = 10):
     return {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4), "steps": steps}
 
 
+def _prologue_figures(t, pro_bytes, pro_traffic, cache):
+    ms = t["median_ms"]
+    rec = {"ms": ms, "cache": cache, "compulsory_bytes": pro_bytes,
+           "gbs": round(pro_bytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(pro_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "counted_bytes": pro_traffic,
+           "counted_gbs": round(pro_traffic / (ms * 1e-3) / 1e9, 1) if pro_traffic else None,
+           "counted_frac_of_hbm_peak": (round(pro_traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                        if pro_traffic else None)}
+    for key in ("min_ms", "calls", "steps"):
+        if key in t:
+            rec[key] = t[key]
+    return rec
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -262,10 +277,12 @@ def cpu_baseline(w, budget_s: float = 12.0, gpu_head=None):
                     "cos_vs_oracle": round(oracle.cosine(got, ref), 8),
                     "bits_equal_frac": round(float(np.mean(got == ref)), 4)}
     return accuracy, {"value": ops / (t_attn + t_share) / 1e12, "unit": "TFLOPS", "cores": nthreads, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"{w.name}: oracle prologue of head (0,0) ({w.S} rows, {t_prep:.2f} s, charged pro rata) + "
                       f"quantized attention of {rows_done} consecutive query rows of that head from a seeded start "
                       f"({t_attn:.2f} s); "
-                      f"{nthreads} threads on {cpu_model()}"}
+                      f"{nthreads} threads (the CPU share one GPU's job is given; the host shows "
+                      f"{os.cpu_count()} CPUs) on {cpu_model()}"}
 
 
 def main():
@@ -361,29 +378,19 @@ def main():
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "attn_kernel", "kernel_ms": round(r["attn_ms"], 4),
                      "algorithmic_per_launch": f"{fl:.4e} ops (4*D ops per query-key pair)"},
-        # the prologue's headline is the prologue as the step runs it, each call right after an
-        # attention launch on the same stream ("in the step"); beside it a call after 512 MiB
-        # were written to flush the memory-side cache (dirty lines of other data in it), and
-        # back-to-back calls on the same inputs, which find part of them in that cache ("warm")
-        "prologue": {"ms": in_step["median_ms"], "min_ms": in_step["min_ms"], "calls": in_step["steps"],
-                     "cache": "as the step leaves it: each call follows an attention launch on the same stream",
-                     "compulsory_bytes": pro_bytes,
-                     "gbs": round(pro_bytes / (in_step["median_ms"] * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(pro_bytes / (in_step["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": pro_traffic,
-                     "achieved_gbs": (round(pro_traffic / (in_step["median_ms"] * 1e-3) / 1e9, 1)
-                                      if pro_traffic else None),
-                     "achieved_frac_of_hbm_peak": (round(pro_traffic / (in_step["median_ms"] * 1e-3) / 1e9
-                                                         / HBM_PEAK_GBS, 4) if pro_traffic else None),
-                     "flushed": {"ms": cold["median_ms"], "min_ms": cold["min_ms"], "calls": cold["calls"],
-                                 "cache": "512 MiB written before each call",
-                                 "gbs": round(pro_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1),
-                                 "achieved_gbs": (round(pro_traffic / (cold["median_ms"] * 1e-3) / 1e9, 1)
-                                                  if pro_traffic else None)},
-                     "warm": {"ms": round(r["prologue_ms"], 4),
-                              "gbs": round(pro_bytes / (r["prologue_ms"] * 1e-3) / 1e9, 1),
-                              "achieved_gbs": (round(pro_traffic / (r["prologue_ms"] * 1e-3) / 1e9, 1)
-                                               if pro_traffic else None)}},
+        # the prologue's headline is a call with the 256 MB memory-side cache flushed first (512 MiB
+        # written before each call, so the inputs come from HBM); beside it the prologue as the step
+        # runs it (each call right after an attention launch on the same stream) and back-to-back
+        # calls on the same inputs, which find part of them in that cache. "gbs" and
+        # "frac_of_hbm_peak" count the compulsory bytes (read Q, K, V once, write the codes once);
+        # "counted_gbs" counts the rocprofv3 bytes (FETCH_SIZE x 2 + WRITE_SIZE, calibrated on a copy),
+        # which are what the L2 fetches and writes, memory-side cache hits included: an upper bound
+        # of the bytes that cross the HBM interface
+        "prologue": _prologue_figures(cold, pro_bytes, pro_traffic, "512 MiB written before each call") | {
+                     "in_step": _prologue_figures(in_step, pro_bytes, pro_traffic,
+                                                  "each call follows an attention launch on the same stream"),
+                     "warm": _prologue_figures({"median_ms": round(r["prologue_ms"], 4)}, pro_bytes, pro_traffic,
+                                               "back-to-back calls on the same inputs")},
         "step_wall_ms": round(r["step_wall_ms"], 4),
         "one_call_at_a_time": one_call_at_a_time(w, 10),
         "other_workloads": others,

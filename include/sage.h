@@ -38,7 +38,8 @@
  *       5. a launch failure -> SAGE_ERR_DEVICE.
  *     sage_last_error() then returns a thread-local message with details.
  *   - An empty problem (B*S*H == 0) returns SAGE_OK without launching.
- *   - Inputs must be finite; non-finite values give unspecified codes.
+ *   - Inputs must be finite (and, with smooth_k, K - k_mean finite in float);
+ *     other values give unspecified codes.
  *
  * Quantized layouts (written by sage_prepare, read by sage_attn). With
  * S_pad = sage_padded_len(S) (S rounded up to whole key tiles of
@@ -82,29 +83,42 @@ typedef struct {
   int64_t stride[4];
 } sage_tensor;
 
-/* Keys per online-softmax tile (128). The tile schedule is part of the
- * result: P is requantized against the running maximum after each tile. */
+/* Keys per online-softmax tile (128). The pages fix an online softmax in
+ * FP32 with P requantized to FP8 (issue, "The kernel") but not its tile size;
+ * 128 is this library's convention, and it is part of the result: P is
+ * requantized against the running maximum after each tile. */
 int sage_kv_tile(void);
 
-/* S rounded up to a multiple of sage_kv_tile(); 0 for S <= 0, -1 when the
- * rounded value does not fit in int64. */
+/* Library convention (layouts above): S rounded up to a multiple of
+ * sage_kv_tile(); 0 for S <= 0, -1 when the rounded value does not fit in
+ * int64. */
 int64_t sage_padded_len(int64_t S);
 
-/* Device workspace sage_prepare needs (per-chunk channel statistics); 0 for
- * an empty or unsupported problem (non-positive size, D not 64 or 128, or a
- * problem past the limits of validation step 2). */
+/* Library convention (the caller owns every buffer): the device workspace
+ * sage_prepare needs (per-chunk channel statistics); 0 for an empty or
+ * unsupported problem (non-positive size, D not 64 or 128, or a problem past
+ * the limits of validation step 2). */
 size_t sage_prepare_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int smooth_k);
 
 /* The prologue (issue, "The kernel"; release notes, "What changed"):
- *   k_mean[b,h,d] = float( sum_s double(K[b,s,h,d]) / S )   (smooth_k; else 0)
+ *   k_mean[b,h,d] = float( fp64(sum_s K[b,s,h,d]) / S )   (smooth_k; else 0)
+ *     where fp64(sum) is the exact sum rounded once to double (nearest, ties
+ *     to even): "summed in fp64", independent of the order of the terms
  *   Q, K' = K - k_mean: per 32-row block a = max|x|, scale = a/127,
  *     code = rint(x * (127/a)) in [-127, 127] (ties to even; a = 0 gives 0)
  *   V: per channel a = max_s |V|, scale = a/448, code = E4M3(v * (448/a))
  *     (round to nearest even; an all-zero channel gives scale 0, codes 0)
- * q, k, v: BF16 tensors of equal size with D = 128. Outputs in the layouts
- * above; k_mean may be NULL. ws: device memory of at least
+ *   A block or channel with a < 2^-64, whose quotient 127/a or 448/a could
+ *   exceed the largest float, is multiplied by 2^64 (exactly) together with a
+ *   before the quotient is formed; wherever the quotient is finite this
+ *   changes no code. The scale stays a/127 (a/448) of the unscaled a.
+ * q, k, v: BF16 tensors of equal size with D = 128 (or 64). Outputs in the
+ * layouts above; k_mean may be NULL. ws: device memory of at least
  * sage_prepare_workspace_bytes() bytes, contents need not be initialised.
- * The result is deterministic and matches the CPU oracle bit for bit. */
+ * Domain: finite inputs and, with smooth_k, K - k_mean finite in float (true
+ * whenever |K| <= 2^126). On it the result is deterministic and every output
+ * (codes, scales, k_mean) matches the CPU oracle bit for bit; outside it the
+ * codes are unspecified. */
 sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
                          float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
                          void* ws, size_t ws_bytes, void* stream);
@@ -144,9 +158,9 @@ sage_status sage_attn_ex(const int8_t* q8, const float* q_scale, const int8_t* k
                          const uint8_t* v8t, const float* v_scale, int64_t B, int64_t S, int64_t H, int64_t D,
                          float sm_scale, int is_causal, const sage_tensor* o, float* lse, void* stream);
 
-/* Device workspace sage_attn_fused needs: the quantized tensors, their
- * scales and the prologue's statistics; 0 when sage_prepare_workspace_bytes
- * would be 0. */
+/* Library convention (the caller owns every buffer): the device workspace
+ * sage_attn_fused needs, i.e. the quantized tensors, their scales and the
+ * prologue's statistics; 0 when sage_prepare_workspace_bytes would be 0. */
 size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /* sage_prepare then sage_attn on one stream: the C image of
@@ -159,9 +173,13 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
                             int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* Library convention: the name of a status code. Errors are returned, never
+ * handled another way, as the issue's package raises instead of falling back
+ * ("What I have so far"). */
 const char* sage_status_string(sage_status s);
 
-/* Thread-local detail of the last error returned on this thread ("" if none). */
+/* Library convention: thread-local detail of the last error returned on this
+ * thread ("" if none). */
 const char* sage_last_error(void);
 
 #ifdef __cplusplus

@@ -79,6 +79,8 @@ def _ptr(a: np.ndarray | None):
 
 
 def threads() -> int:
+    """Worker threads: the host's CPUs, at most 16 (the CPU share a one-GPU
+    job is given on the machines this runs on, whatever the host shows)."""
     return max(1, min(16, os.cpu_count() or 1))
 
 

@@ -21,6 +21,7 @@ softmax_scale, ...)):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -169,6 +170,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _alloc_on(stream):
+    """Allocate on the stream the library will use: torch's caching allocator
+    then reuses a freed block only behind that stream's pending work (a
+    temporary allocated on the current stream but used on another could be
+    handed out again while the other stream still reads it)."""
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None, reuse: dict | None = None) -> dict:
     """Run the prologue; returns the quantized tensors in the library's layouts.
 
@@ -196,20 +206,26 @@ def _prepare(q, k, v, smooth_k, layout, stream, reuse):
         out = reuse
         ws = reuse["_ws"]
     else:
-        out = dict(q8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-                   q_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-                   k8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-                   k_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-                   v8t=torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
-                   v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev),
-                   k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev))
-        ws = torch.empty(max(int(nws), 1), dtype=torch.uint8, device=dev)
+        with _alloc_on(stream):
+            out = _alloc_prepared(B, S, H, D, Sp, dev)
+            ws = torch.empty(max(int(nws), 1), dtype=torch.uint8, device=dev)
     check(L.sage_prepare(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), int(bool(smooth_k)), _ptr(out["q8"]),
                          _ptr(out["q_scale"]), _ptr(out["k8"]), _ptr(out["k_scale"]), _ptr(out["v8t"]),
                          _ptr(out["v_scale"]), _ptr(out["k_mean"]), _ptr(ws), nws, _stream(stream)))
     out["S"] = S
     out["_ws"] = ws   # keep the workspace alive until the stream is done with it
     return out
+
+
+def _alloc_prepared(B, S, H, D, Sp, dev):
+    import torch
+    return dict(q8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+                q_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+                k8=torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
+                k_scale=torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
+                v8t=torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
+                v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev),
+                k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev))
 
 
 def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = False, lse=None,
@@ -227,13 +243,14 @@ def _attn(prep, sm_scale, out, stream, return_lse, lse, is_causal):
     import torch
     B, H, Sp, D = prep["q8"].shape
     S = prep["S"]
-    if out is None:
-        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=prep["q8"].device)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=prep["q8"].device)
+        if return_lse and lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=prep["q8"].device)
     to = describe(out)
     args = (_ptr(prep["q8"]), _ptr(prep["q_scale"]), _ptr(prep["k8"]), _ptr(prep["k_scale"]), _ptr(prep["v8t"]),
             _ptr(prep["v_scale"]), B, S, H, D, float(sm_scale), ctypes.byref(to))
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=prep["q8"].device)
     if is_causal:
         check(lib().sage_attn_ex(*args[:11], 1, args[11], _ptr(lse) if return_lse else None, _stream(stream)))
     elif not return_lse:
@@ -267,15 +284,16 @@ def _sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse, smooth_k,
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     tq, tk, tv = describe(q, tensor_layout), describe(k, tensor_layout), describe(v, tensor_layout)
-    if out is None:
-        out = torch.empty_like(q)
-    to = describe(out, tensor_layout)
     B, S, H, D = tq.size
     L = lib()
     nws = int(L.sage_fused_workspace_bytes(B, S, H, D))
-    if workspace is None:
-        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if return_lse else None
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if return_lse else None
+    to = describe(out, tensor_layout)
     check(L.sage_attn_fused(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), int(bool(is_causal)),
                             float(sm_scale), int(bool(return_lse)), _ptr(lse), int(bool(smooth_k)), _ptr(workspace),
                             workspace.numel(), _stream(stream)))

@@ -206,13 +206,24 @@ SAGE_INLINE float block_max(const v16i& x, float c) {
   return (float)im * c;
 }
 
-// Probabilities of 4 consecutive keys (group g of block kb): 448 p = exp2(t - moff)
-// with t = float(acc) * c, summed into ps, packed to FP8 into pk.
+// Probabilities of 4 consecutive keys (group g of block kb), 448 p for the
+// score t = float(acc) * c, summed into ps, packed to FP8 into pk.
+// Fast form (kExact false, moff = m' - log2 448): 448 p = exp2(acc c - moff) in
+// one FMA, without the method's rounding of t to float first. That rounding
+// moves the exponent by at most half an ulp of t: negligible while |t| is
+// moderate, whole units once |t| passes 2^24, where the FMA form can even
+// exceed 448 (an FP8 NaN). Waves whose scores may reach 2^14 in magnitude
+// therefore take the exact form (kExact true, moff = m'): the method's own
+// steps, p = exp2(t - m') with t rounded to float first, then 448 p.
+template <bool kExact>
 SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v8i (&pk)[2], float (&ps)[4]) {
   float p[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[4 * g + u], c, -moff));
+    if constexpr (kExact)   // a product, then a difference: no contraction (-ffp-contract=off)
+      p[u] = 448.0f * __builtin_amdgcn_exp2f((float)sc[4 * g + u] * c - moff);
+    else
+      p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[4 * g + u], c, -moff));
     ps[u] += p[u];
   }
   const int j = 16 * (kb & 1) + 4 * g;   // k-slot of p[0] within the 64-key half-tile
@@ -254,7 +265,7 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
 // blocks no lane of the wave sees; each lane then has at most one partly
 // masked block, whose masked keys' probability comes off l as above. Their
 // FP8 codes, which meet real V codes there, are cleared before that tile's PV.
-template <int D, bool kHasPrev>
+template <int D, bool kHasPrev, bool kExact>
 SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4], const float (&cblk)[4],
                                 bool masked, int lim, const uint8_t* vbuf_prev, const uint8_t* kbuf_next,
                                 const uint8_t* qrow, int half, int col, int prow) {
@@ -314,7 +325,7 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
   }
   float m_new, alpha, moff;
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#define SAGE_EXP(KB_, G_) exp_group(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
+#define SAGE_EXP(KB_, G_) exp_group<kExact>(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
 #define SAGE_L_UPDATE()                                                                               \
   {                                                                                                   \
     float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                   \
@@ -322,7 +333,8 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
       const int kbp = lim >> 5; /* the partly masked block */                                         \
       const int nmask = min(16, max(0, 32 * kbp + kbase + 16 - lim));                                 \
       const float ck = cblk[kbp];                                                                     \
-      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, ck, -moff));           \
+      const float pm = kExact ? 448.0f * __builtin_amdgcn_exp2f((float)INT32_MIN * ck - moff)         \
+                              : __builtin_amdgcn_exp2f(__builtin_fmaf((float)INT32_MIN, ck, -moff));  \
       if (nmask > 0) psum -= (float)nmask * pm;                                                       \
     }                                                                                                 \
     st.l_run = alpha * st.l_run + psum;                                                               \
@@ -336,7 +348,7 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
     tmax = max_xor32(tmax);
     m_new = fmaxf(st.m_run, tmax);
     alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
-    moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
+    moff = kExact ? m_new : m_new - kLog2_448;          // see exp_group
   })
   // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
   SAGE_PV_SLOT(4, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
@@ -350,7 +362,7 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
     tmax = max_xor32(tmax);
     m_new = fmaxf(st.m_run, tmax);
     alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first tile
-    moff = m_new - kLog2_448;                           // exp2(t - moff) = 448 p
+    moff = kExact ? m_new : m_new - kLog2_448;          // see exp_group
   })
   // pk[0] of the previous tile has been handed to its MFMAs: blocks 0, 1 may overwrite it
   SAGE_PV_SLOT(2, { SAGE_EXP(0, 0); SAGE_EXP(0, 1); })
@@ -427,6 +439,117 @@ SAGE_INLINE void pv_tile(WaveState<D>& st, const uint8_t* vbuf, int half, int co
                                                                    st.oacc[d], 0, 0, 0, 0, 0, 0);
 }
 
+// The key loop of one wave, its tail and the epilogue: the online softmax
+// state starts here, so the two copies (fast and exact form) share no state
+// and are register-allocated independently.
+template <int D, bool kCausal, bool kExact>
+SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                          const uint32_t (&k_lane_off)[Dim<D>::kCopyInstr],
+                          const uint32_t (&v_lane_off)[Dim<D>::kCopyInstr], const float* ks, float qs, float sl2,
+                          const uint8_t* qrow, int prow, int wave, int half, int col, int ntw, int ntiles,
+                          int last_valid, uint32_t spad32, int64_t q0, int64_t S, int64_t bh, int64_t b, int64_t h,
+                          const float* __restrict__ v_scale, const Bf16OutView& o, float* __restrict__ lse) {
+  using Dm = Dim<D>;
+  constexpr int TB = Dm::kTileBytes;
+#define KBUF(i) (lds + (i) * TB)
+#define VBUF(i) (lds + (2 + (i)) * TB)
+  WaveState<D> st;
+#pragma unroll
+  for (int d = 0; d < Dm::kOBlk; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st.oacc[d][v] = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.pk[kc][i] = 0;
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+
+  v16i sa[4], sb[4];   // scores of the current and the next tile; they swap roles every iteration
+  qk_tile<D>(sa, KBUF(0), qrow, half, col, prow);
+  float4 ksv = *reinterpret_cast<const float4*>(ks);   // k_scale of the four blocks of the current tile
+
+  // Iteration t: PV of tile t-1, softmax of tile t, scores of tile t+1. On
+  // entry K(t+1) and V(t-1) must be in LDS; K(t+2) goes to the buffer K(t)
+  // occupied and V(t) to the one V(t-2) occupied. After the last tile the
+  // score MFMAs read stale K bytes whose scores are never used.
+  // Causal: the last visited tile holds the workgroup's own queries; there
+  // the lane sees keys below min(32 wave + col + 1, nvalid), and blocks at or
+  // past min(32 (wave + 1), nvalid) are masked for the whole wave.
+#define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                     \
+  {                                                                                                          \
+    const int t_ = (T_);                                                                                     \
+    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                    \
+    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                \
+    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                   \
+    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                 \
+    const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                              \
+    const bool diag = kCausal && t_ == ntw - 1;                                                              \
+    const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                           \
+    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                       \
+    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */ \
+    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;             \
+    if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                             \
+    tile_iteration<D, HAS_PREV_, kExact>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                    \
+                                         diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1), \
+                                         KBUF((PAR_) ^ 1), qrow, half, col, prow);                           \
+  }
+  // tile t uses buffer pair t & 1; the parity is spelled out so that buffer
+  // addresses fold into the LDS instructions' offsets (t is odd in the loop)
+  SAGE_ITERATION(0, 0, false, sa, sb)
+  int t = 1;
+  for (; t + 1 < ntw; t += 2) {
+    SAGE_ITERATION(t, 1, true, sb, sa)
+    SAGE_ITERATION(t + 1, 0, true, sa, sb)
+  }
+  if (t < ntw) SAGE_ITERATION(t, 1, true, sb, sa)
+#undef SAGE_ITERATION
+  if constexpr (kCausal) {
+    // Clear the FP8 codes of the diagonal tile's masked keys (those at or past
+    // lim), whose V codes are real: byte u of pk[kc][i] is key
+    // 32 kb + 16 half + 4 g + u of the tile, kb = 2 kc + i / 4, g = i % 4.
+    const int lim = min(32 * wave + col + 1, ntw == ntiles ? last_valid : kKvTile);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int base = 32 * (2 * kc + i / 4) + 16 * half + 4 * (i % 4);
+        const int nb = min(4, max(0, lim - base));   // valid bytes of the word
+        const uint32_t keep = nb == 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
+        st.pk[kc][i] &= (int)keep;
+      }
+  }
+  // PV of the last tile
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  pv_tile<D>(st, VBUF((ntw - 1) & 1), half, col);
+
+  // ---- epilogue: O = o * v_scale / (448 l)
+  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+  const float inv_l = 1.0f / l_tot;
+  const int64_t qi = q0 + col;
+  // log-sum-exp of the row's dequantized scores, natural log: l_tot = 448 sum_j 2^(t_j - m)
+  if (lse != nullptr && half == 0 && qi < S) lse[bh * S + qi] = (st.m_run + __log2f(l_tot) - kLog2_448) * kLn2;
+  if (qi < S) {
+    uint16_t* orow = o.data + b * o.sb + qi * o.ss + h * o.sh;
+    const float* vs = v_scale + bh * D;
+#pragma unroll
+    for (int d = 0; d < Dm::kOBlk; ++d) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int ch = 32 * d + 8 * a + 4 * half;
+        const float4 sc = *reinterpret_cast<const float4*>(vs + ch);
+        uint2 w;
+        w.x = pack_bf16x2(st.oacc[d][4 * a + 0] * sc.x * inv_l, st.oacc[d][4 * a + 1] * sc.y * inv_l);
+        w.y = pack_bf16x2(st.oacc[d][4 * a + 2] * sc.z * inv_l, st.oacc[d][4 * a + 3] * sc.w * inv_l);
+        *reinterpret_cast<uint2*>(orow + ch) = w;
+      }
+    }
+  }
+#undef KBUF
+#undef VBUF
+}
+
 template <int D, bool kCausal>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, const int8_t* __restrict__ k8,
@@ -492,6 +615,11 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
     v_lane_off[i] = (uint32_t)(lane >> 3) * spad32 + (uint32_t)(((lane & 7) ^ (((lane >> 4) & 3) | ((i & 1) << 2))) * 16);
   const float* ks = k_scale + bh * (S_pad / kQBlock);
   float qs = active ? q_scale[bh * (S_pad / kQBlock) + q0 / kQBlock] : 0.0f;
+  // Key-block scale from which this wave's scores may reach 2^14 in magnitude
+  // (|acc| <= 128 * 127^2 < 2^21), as float bits (scales are >= 0, so their
+  // bits order like their values). Ordinary inputs stay far below it (scores of
+  // tens); q_scale 0 gives +inf (never reached).
+  const uint32_t kexact = __builtin_amdgcn_readfirstlane(__float_as_uint(0x1p-7f / (sl2 * qs)));
   // kept in a vector register: a VALU operation reads at most one scalar
   // register, and the key-block scales arrive in scalar registers
   asm volatile("" : "+v"(qs));
@@ -513,18 +641,6 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // A-operand row of the score MFMA fed by this lane: key pi(col) of a 32-key block
   const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
 
-  WaveState<D> st;
-#pragma unroll
-  for (int d = 0; d < Dm::kOBlk; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) st.oacc[d][v] = 0.0f;
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.pk[kc][i] = 0;
-  st.m_run = -INFINITY;
-  st.l_run = 0.0f;
-
   const int ntiles = (int)(S_pad / kKvTile);
   const int last_valid = (int)(S - (int64_t)(ntiles - 1) * kKvTile);   // valid keys in the last tile (1..128)
   // key tiles this workgroup visits: causal stops at the tile of its own
@@ -535,89 +651,23 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   // K(0), K(1) in; scores of tile 0.
   load_k<D>(KBUF(0), rk, 0, k_lane_off, wave);
   if (ntw > 1) load_k<D>(KBUF(1), rk, 1, k_lane_off, wave);
+  // The largest key-block scale this wave meets (bits; scales are >= 0), read
+  // while the tiles load: at or above kexact the wave runs the exact form of
+  // the softmax step (see exp_group) in its own copy of the key loop. The two
+  // copies pass the same barriers, so the waves of a workgroup may differ.
+  uint32_t kmax = 0;
+  for (int i = lane; i < 4 * ntw; i += 64) kmax = max(kmax, __float_as_uint(ks[i]));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  v16i sa[4], sb[4];   // scores of the current and the next tile; they swap roles every iteration
-  qk_tile<D>(sa, KBUF(0), qrow, half, col, prow);
-  float4 ksv = *reinterpret_cast<const float4*>(ks);   // k_scale of the four blocks of the current tile
-
-  // Iteration t: PV of tile t-1, softmax of tile t, scores of tile t+1. On
-  // entry K(t+1) and V(t-1) must be in LDS; K(t+2) goes to the buffer K(t)
-  // occupied and V(t) to the one V(t-2) occupied. After the last tile the
-  // score MFMAs read stale K bytes whose scores are never used.
-  // Causal: the last visited tile holds the workgroup's own queries; there
-  // the lane sees keys below min(32 wave + col + 1, nvalid), and blocks at or
-  // past min(32 (wave + 1), nvalid) are masked for the whole wave.
-#define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                     \
-  {                                                                                                          \
-    const int t_ = (T_);                                                                                     \
-    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                    \
-    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                \
-    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                   \
-    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                 \
-    const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                              \
-    const bool diag = kCausal && t_ == ntw - 1;                                                              \
-    const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                           \
-    const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                       \
-    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */ \
-    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;             \
-    if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                             \
-    tile_iteration<D, HAS_PREV_>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                            \
-                                 diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1),         \
-                                 KBUF((PAR_) ^ 1), qrow, half, col, prow);                                   \
+  if (__builtin_expect(__builtin_amdgcn_readfirstlane(kmax) >= kexact, 0)) {
+    key_loop<D, kCausal, true>(lds, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
+                               ntiles, last_valid, spad32, q0, S, bh, b, h, v_scale, o, lse);
+    return;
   }
-  // tile t uses buffer pair t & 1; the parity is spelled out so that buffer
-  // addresses fold into the LDS instructions' offsets (t is odd in the loop)
-  SAGE_ITERATION(0, 0, false, sa, sb)
-  int t = 1;
-  for (; t + 1 < ntw; t += 2) {
-    SAGE_ITERATION(t, 1, true, sb, sa)
-    SAGE_ITERATION(t + 1, 0, true, sa, sb)
-  }
-  if (t < ntw) SAGE_ITERATION(t, 1, true, sb, sa)
-#undef SAGE_ITERATION
-  if constexpr (kCausal) {
-    // Clear the FP8 codes of the diagonal tile's masked keys (those at or past
-    // lim), whose V codes are real: byte u of pk[kc][i] is key
-    // 32 kb + 16 half + 4 g + u of the tile, kb = 2 kc + i / 4, g = i % 4.
-    const int lim = min(32 * wave + col + 1, ntw == ntiles ? last_valid : kKvTile);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int base = 32 * (2 * kc + i / 4) + 16 * half + 4 * (i % 4);
-        const int nb = min(4, max(0, lim - base));   // valid bytes of the word
-        const uint32_t keep = nb == 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
-        st.pk[kc][i] &= (int)keep;
-      }
-  }
-  // PV of the last tile
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  pv_tile<D>(st, VBUF((ntw - 1) & 1), half, col);
-
-  // ---- epilogue: O = o * v_scale / (448 l)
-  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
-  const float inv_l = 1.0f / l_tot;
-  const int64_t qi = q0 + col;
-  // log-sum-exp of the row's dequantized scores, natural log: l_tot = 448 sum_j 2^(t_j - m)
-  if (lse != nullptr && half == 0 && qi < S) lse[bh * S + qi] = (st.m_run + __log2f(l_tot) - kLog2_448) * kLn2;
-  if (qi < S) {
-    uint16_t* orow = o.data + b * o.sb + qi * o.ss + h * o.sh;
-    const float* vs = v_scale + bh * D;
-#pragma unroll
-    for (int d = 0; d < Dm::kOBlk; ++d) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int ch = 32 * d + 8 * a + 4 * half;
-        const float4 sc = *reinterpret_cast<const float4*>(vs + ch);
-        uint2 w;
-        w.x = pack_bf16x2(st.oacc[d][4 * a + 0] * sc.x * inv_l, st.oacc[d][4 * a + 1] * sc.y * inv_l);
-        w.y = pack_bf16x2(st.oacc[d][4 * a + 2] * sc.z * inv_l, st.oacc[d][4 * a + 3] * sc.w * inv_l);
-        *reinterpret_cast<uint2*>(orow + ch) = w;
-      }
-    }
-  }
+  key_loop<D, kCausal, false>(lds, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
+                              ntiles, last_valid, spad32, q0, S, bh, b, h, v_scale, o, lse);
 #undef KBUF
 #undef VBUF
 }

@@ -20,8 +20,9 @@
 //            first; V codes are transposed through LDS into channel-major rows.
 // Every address is computed in 64-bit arithmetic from 64-bit strides.
 // Rounding follows the method's reading exactly (IEEE float division and
-// multiply, rint, hardware E4M3 conversion with round to nearest even), so the
-// codes and scales are bit-identical to the CPU oracle's.
+// multiply, rint, hardware E4M3 conversion with round to nearest even, the
+// key channel sum exact before its one rounding to double), so the codes,
+// scales and key means are bit-identical to the CPU oracle's.
 #include "sage_internal.hpp"
 
 namespace sage {
@@ -61,6 +62,20 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+constexpr float kTiny = 0x1p-64f;       // blocks and channels below this absmax are lifted
+constexpr float kTinyLift = 0x1p64f;    // by this exact factor before 127/a or 448/a
+
+// a + b when that sum is a double, else NaN (which every later addition keeps).
+// If the sum is exact, s - a = b and s - b = a exactly. If it is not, then for
+// the operand of larger magnitude, say a, s - a is computed exactly (it
+// recovers the rounding error of s, Dekker's Fast2Sum) and differs from b.
+// Summing key channels with it in any order therefore gives either the exact
+// sum, which is then also the sum rounded once, or NaN.
+__device__ inline double add_exact_or_nan(double a, double b) {
+  const double s = a + b;
+  return (s - a == b && s - b == a) ? s : __longlong_as_double(0x7FF8000000000000ll);
+}
+
 // Lane geometry of one wave over a 32-row block of D channels: lane (c, g),
 // c = lane % L, g = lane / L, holds channels 8c .. 8c+7 of rows G*i + g,
 // i = 0 .. I-1 (L lanes per row, G row groups, I rows per lane).
@@ -75,7 +90,7 @@ struct Geo {
 // (row G*i + g, channel 8c + e); invalid rows hold 0.
 // Writes the 32 rows of codes and the block's scale.
 template <int D>
-__device__ inline void quant_block_store(const float (&x)[8 * Geo<D>::I], int8_t* dst_rows, float* scale_out,
+__device__ inline void quant_block_store(float (&x)[8 * Geo<D>::I], int8_t* dst_rows, float* scale_out,
                                          int lane) {
   using Gm = Geo<D>;
   float a = 0.0f;
@@ -85,7 +100,17 @@ __device__ inline void quant_block_store(const float (&x)[8 * Geo<D>::I], int8_t
   float scale = 0.0f, inv = 0.0f;
   if (a != 0.0f) {
     scale = a / 127.0f;   // correctly rounded IEEE division
-    inv = 127.0f / a;
+    // A block of tiny values (a < 2^-64, where 127/a may exceed the largest
+    // float) is lifted by 2^64, exactly, before the quotient is formed; the
+    // codes are those of the unlifted form wherever its quotient is finite.
+    // The branch is uniform over the wave (a is the block's maximum).
+    if (a < kTiny) {
+#pragma unroll
+      for (int i = 0; i < 8 * Gm::I; ++i) x[i] *= kTinyLift;
+      inv = 127.0f / (a * kTinyLift);
+    } else {
+      inv = 127.0f / a;
+    }
   }
   const int c = lane % Gm::L, g = lane / Gm::L;
 #pragma unroll
@@ -147,7 +172,7 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 #pragma unroll
       for (int i = 0; i < Gm::I; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ksum[e] += (double)x[i * 8 + e];
+        for (int e = 0; e < 8; ++e) ksum[e] = add_exact_or_nan(ksum[e], (double)x[i * 8 + e]);
     } else {
       quant_block_store<D>(x, k8 + (bh * S_pad + r0) * D, k_scale + bh * (S_pad / kQBlock) + blk, lane);
     }
@@ -164,12 +189,13 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
 
   // Fold the row groups of the wave (lanes c, c + L, c + 2L, ...), then the
-  // four waves, always in the same order.
+  // four waves. Every key-sum addition is checked: an inexact one turns the
+  // partial into NaN, and the finalize kernel then sums that channel exactly.
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
 #pragma unroll
     for (int m = Gm::L; m < 64; m <<= 1) {
-      ksum[e] += __shfl_xor(ksum[e], m, 64);
+      ksum[e] = add_exact_or_nan(ksum[e], __shfl_xor(ksum[e], m, 64));
       vmax[e] = fmaxf(vmax[e], __shfl_xor(vmax[e], m, 64));
     }
   }
@@ -181,7 +207,8 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
   __syncthreads();
   if (tid < D) {
-    double s = ((s_sum[0][tid] + s_sum[1][tid]) + s_sum[2][tid]) + s_sum[3][tid];
+    double s = add_exact_or_nan(add_exact_or_nan(add_exact_or_nan(s_sum[0][tid], s_sum[1][tid]), s_sum[2][tid]),
+                                s_sum[3][tid]);
     float m = fmaxf(fmaxf(s_max[0][tid], s_max[1][tid]), fmaxf(s_max[2][tid], s_max[3][tid]));
     ksum_part[(bh * nparts + part) * D + tid] = s;
     vmax_part[(bh * nparts + part) * D + tid] = m;
@@ -193,44 +220,159 @@ stats_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 // are folded in slice order. The order is fixed, so the result is the same on
 // every run.
 constexpr int kFinalizeSlices = 8;
+// Exact channel sums: a finite BF16 value is M * 2^(e - 133) with integers
+// 0 <= M < 256 and 0 <= e <= 253 (exponent field E > 0: M = 128 + mantissa,
+// e = E - 1; E = 0: M = mantissa, e = 0), so a channel's sum over fewer than
+// 2^25 rows is an integer multiple of 2^-133 below 2^286 in magnitude: nine
+// 32-bit digits of a two's complement integer hold it.
+constexpr int kDigits = 9;
+
+// Threads of this many slices form the exact sums (their digit words share
+// the workgroup's LDS with the fold of the partials).
+constexpr int kExactSlices = 4;
+
+// Channel d's exact key sum over rows s = j, j + kExactSlices, ..., accumulated
+// by thread (d, j) into its own 64-bit words w(j, 0..8, d) (one word per 32-bit
+// digit, carries left for later: a word receives at most 2^23 additions below
+// 2^32 each); the caller adds the slices and rounds.
+__device__ inline void exact_sum_rows(const uint16_t* kcol, int64_t ss, int64_t S, int j, long long* dig_j_d,
+                                      int dstride) {
+  for (int64_t s = j; s < S; s += kExactSlices) {
+    const uint32_t b = kcol[s * ss];
+    const uint32_t E = (b >> 7) & 0xFFu, M = E ? 128u + (b & 0x7Fu) : (b & 0x7Fu);
+    if (M == 0) continue;
+    const int e = E ? (int)E - 1 : 0;
+    const unsigned long long w = (unsigned long long)M << (e & 31);   // below 2^39
+    long long lo = (long long)(w & 0xFFFFFFFFull), hi = (long long)(w >> 32);
+    if (b & 0x8000u) { lo = -lo; hi = -hi; }
+    dig_j_d[(e >> 5) * dstride] += lo;
+    dig_j_d[((e >> 5) + 1) * dstride] += hi;
+  }
+}
+
+// The integer sum_k w[k] 2^(32k) (w[k] the digit words of all slices added,
+// each below 2^57 in magnitude) times 2^-133, rounded once to double.
+// Fully unrolled, so the digits stay in registers.
+__device__ inline double digits_to_double(const long long (&w)[kDigits]) {
+  uint32_t dig[kDigits];
+  long long carry = 0;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) {
+    const long long t = w[k] + carry;
+    dig[k] = (uint32_t)(t & 0xFFFFFFFFll);
+    carry = t >> 32;   // arithmetic shift: floor division by 2^32
+  }
+  // carry is now the sign extension above 288 bits: 0 or -1
+  const bool negative = carry < 0;
+  if (negative) {   // two's complement negation of the 288-bit integer
+    unsigned long long c = 1;
+#pragma unroll
+    for (int k = 0; k < kDigits; ++k) {
+      const unsigned long long t = (unsigned long long)(~dig[k]) + c;
+      dig[k] = (uint32_t)t;
+      c = t >> 32;
+    }
+  }
+  int top = -1;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) top = dig[k] != 0 ? k : top;
+  if (top < 0) return 0.0;
+  // The 64 bits from the most significant one down, from digits top, top - 1
+  // and top - 2, with every bit below them ORed into bit 0 (below the rounding
+  // position of a 53-bit significand, so the conversion rounds once, correctly).
+  unsigned long long hi = 0, mid = 0, lo = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) {
+    hi = k == top ? dig[k] : hi;
+    mid = k == top - 1 ? dig[k] : mid;
+    lo = k == top - 2 ? dig[k] : lo;
+    sticky |= k < top - 2 && dig[k] != 0;
+  }
+  const int msb = 31 - __clz((int)hi);
+  unsigned long long u = (hi << (63 - msb)) | (mid << (31 - msb)) | (lo >> (msb + 1));
+  sticky |= (lo & ((1ull << (msb + 1)) - 1)) != 0;
+  u |= sticky ? 1ull : 0ull;
+  const int low_bit = 32 * (top - 2) + msb + 1;   // weight of u's bit 0, in units of 2^-133
+  const double m = ldexp((double)u, low_bit - 133);
+  return negative ? -m : m;
+}
 
 template <int D>
 __global__ void __launch_bounds__(D * kFinalizeSlices)
-finalize_kernel(int64_t S, int64_t nparts, int smooth_k, const double* __restrict__ ksum_part,
+finalize_kernel(Bf16View k, int64_t H, int64_t S, int64_t nparts, int smooth_k, const double* __restrict__ ksum_part,
                 const float* __restrict__ vmax_part, float* __restrict__ kmean, float* __restrict__ vinv,
-                float* __restrict__ v_scale, float* __restrict__ k_mean_out) {
+                float* __restrict__ vlift, float* __restrict__ v_scale, float* __restrict__ k_mean_out) {
   const int64_t bh = blockIdx.x;
   const int d = threadIdx.x % D, j = threadIdx.x / D;
   double s = 0.0;
   float a = 0.0f;
 #pragma unroll 8
   for (int64_t p = j; p < nparts; p += kFinalizeSlices) {
-    s += ksum_part[(bh * nparts + p) * D + d];
+    s = add_exact_or_nan(s, ksum_part[(bh * nparts + p) * D + d]);
     a = fmaxf(a, vmax_part[(bh * nparts + p) * D + d]);
   }
-  __shared__ double s_sum[kFinalizeSlices][D];
-  __shared__ float s_max[kFinalizeSlices][D];
-  s_sum[j][d] = s;
-  s_max[j][d] = a;
+  // the fold of the partials, then (only if needed) the exact sums' digit words
+  __shared__ union {
+    struct {
+      double sum[kFinalizeSlices][D];
+      float max[kFinalizeSlices][D];
+    } fold;
+    long long dig[kExactSlices][kDigits][D];
+  } sh;
+  sh.fold.sum[j][d] = s;
+  sh.fold.max[j][d] = a;
   __syncthreads();
-  if (j != 0) return;
+  s = sh.fold.sum[0][d];
+  a = sh.fold.max[0][d];
 #pragma unroll
   for (int i = 1; i < kFinalizeSlices; ++i) {
-    s += s_sum[i][d];
-    a = fmaxf(a, s_max[i][d]);
+    s = add_exact_or_nan(s, sh.fold.sum[i][d]);
+    a = fmaxf(a, sh.fold.max[i][d]);
   }
+  // A NaN sum means some fp64 addition on the way was inexact: that channel's
+  // sum is then formed exactly from K itself (the same value the fp64 sum has
+  // whenever it is exact). Rare in practice; uniform over the workgroup. The
+  // barrier also ends every read of the fold before the digits reuse its LDS.
+  const bool redo = smooth_k && s != s;
+  if (__syncthreads_or(redo)) {
+    if (j < kExactSlices) {
+#pragma unroll
+      for (int kk = 0; kk < kDigits; ++kk) sh.dig[j][kk][d] = 0;
+      if (redo) {
+        const int64_t b = bh / H, h = bh % H;
+        exact_sum_rows(k.data + b * k.sb + h * k.sh + d, k.ss, S, j, &sh.dig[j][0][d], D);
+      }
+    }
+    __syncthreads();
+    if (redo) {
+      long long w[kDigits];
+#pragma unroll
+      for (int kk = 0; kk < kDigits; ++kk) {
+        long long t = 0;
+#pragma unroll
+        for (int i = 0; i < kExactSlices; ++i) t += sh.dig[i][kk][d];
+        w[kk] = t;
+      }
+      s = digits_to_double(w);
+    }
+  }
+  if (j != 0) return;
   float km = smooth_k ? (float)(s / (double)S) : 0.0f;
   kmean[bh * D + d] = km;
   if (k_mean_out) k_mean_out[bh * D + d] = km;
   v_scale[bh * D + d] = a == 0.0f ? 0.0f : a / 448.0f;
-  vinv[bh * D + d] = a == 0.0f ? 0.0f : 448.0f / a;
+  // a channel of tiny values is lifted by 2^64 before 448/a, as an INT8 block is
+  const float lift = a < kTiny ? kTinyLift : 1.0f;
+  vinv[bh * D + d] = a == 0.0f ? 0.0f : 448.0f / (a * lift);
+  vlift[bh * D + d] = lift;
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int smooth_k,
-             const float* __restrict__ kmean, const float* __restrict__ vinv, int8_t* __restrict__ k8,
-             float* __restrict__ k_scale, uint8_t* __restrict__ v8t) {
+             const float* __restrict__ kmean, const float* __restrict__ vinv, const float* __restrict__ vlift,
+             int8_t* __restrict__ k8, float* __restrict__ k_scale, uint8_t* __restrict__ v8t) {
   using Gm = Geo<D>;
   __shared__ uint32_t tile[D * kVTileStride / 4];   // [channel][row] codes, 132-byte rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -269,9 +411,21 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
   // one dword.
   {
     const uint16_t* vb = v.data + b * v.sb + h * v.sh + 8 * c;
-    float inv[8];
+    float inv[8], lift[8];
+    uint32_t keep[8];   // an all-zero channel (scale 0) gets codes 0, also for its -0 entries
 #pragma unroll
-    for (int e = 0; e < 8; ++e) inv[e] = vinv[bh * D + 8 * c + e];
+    for (int e = 0; e < 8; ++e) {
+      inv[e] = vinv[bh * D + 8 * c + e];
+      lift[e] = vlift[bh * D + 8 * c + e];
+      keep[e] = inv[e] != 0.0f ? 0xFFFFFFFFu : 0u;
+    }
+    // channels of tiny values are lifted by 2^64 before the scaling (their
+    // quotient was formed from the lifted maximum); the factor is applied only
+    // when some channel of the wave needs it
+    bool lifted = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lifted |= lift[e] != 1.0f;
+    lifted = __builtin_amdgcn_ballot_w64(lifted) != 0;
 #pragma unroll
     for (int half = 0; half < 8 / Gm::G; ++half) {
       const int rl = 32 * wave + 4 * Gm::G * half + 4 * g;   // local row of j = 0
@@ -287,6 +441,10 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = 0.0f;
         }
+        if (lifted) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= lift[e];
+        }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           // E4M3 with round to nearest even; |y * inv| <= 448 (1 + 2^-23) never overflows
@@ -296,7 +454,7 @@ quant_kernel(Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int sm
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[((8 * c + e) * kVTileStride + rl) / 4] = codes[e];
+      for (int e = 0; e < 8; ++e) tile[((8 * c + e) * kVTileStride + rl) / 4] = codes[e] & keep[e];
     }
   }
   __syncthreads();
@@ -323,12 +481,13 @@ hipError_t launch_prologue_d(const Bf16View& q, const Bf16View& k, const Bf16Vie
                      ws.vmax_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel<D>, dim3((unsigned)BH), dim3(D * kFinalizeSlices), 0, stream, ps.S, ps.nparts,
-                     smooth_k, ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, v_scale, k_mean_out);
+  hipLaunchKernelGGL(finalize_kernel<D>, dim3((unsigned)BH), dim3(D * kFinalizeSlices), 0, stream, k, ps.H, ps.S,
+                     ps.nparts, smooth_k, ws.ksum_part, ws.vmax_part, ws.kmean, ws.vinv, ws.vlift, v_scale,
+                     k_mean_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(quant_kernel<D>, dim3((unsigned)(BH * nchunks)), dim3(kThreads), 0, stream, k, v, ps.H, ps.S,
-                     ps.S_pad, smooth_k, ws.kmean, ws.vinv, k8, k_scale, v8t);
+                     ps.S_pad, smooth_k, ws.kmean, ws.vinv, ws.vlift, k8, k_scale, v8t);
   return hipGetLastError();
 }
 
@@ -352,7 +511,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t prologue_ws_bytes(const PrologueShape& ps) {
   const size_t bh = (size_t)(ps.B * ps.H), D = (size_t)ps.D;
   return align256(bh * ps.nparts * D * sizeof(double)) + align256(bh * ps.nparts * D * sizeof(float)) +
-         2 * align256(bh * D * sizeof(float));
+         3 * align256(bh * D * sizeof(float));
 }
 
 PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps) {
@@ -362,7 +521,8 @@ PrologueWs prologue_ws_carve(void* ws, const PrologueShape& ps) {
   w.ksum_part = reinterpret_cast<double*>(p); p += align256(bh * ps.nparts * D * sizeof(double));
   w.vmax_part = reinterpret_cast<float*>(p); p += align256(bh * ps.nparts * D * sizeof(float));
   w.kmean = reinterpret_cast<float*>(p); p += align256(bh * D * sizeof(float));
-  w.vinv = reinterpret_cast<float*>(p);
+  w.vinv = reinterpret_cast<float*>(p); p += align256(bh * D * sizeof(float));
+  w.vlift = reinterpret_cast<float*>(p);
   return w;
 }
 

@@ -41,7 +41,8 @@ struct PrologueWs {
   double* ksum_part;   // [B*H][nparts][128]
   float* vmax_part;    // [B*H][nparts][128]
   float* kmean;        // [B*H][128]
-  float* vinv;         // [B*H][128]
+  float* vinv;         // [B*H][128]  448 / (amax * lift)
+  float* vlift;        // [B*H][128]  2^64 for a channel with amax < 2^-64, else 1
 };
 
 struct PrologueShape {

@@ -3,10 +3,12 @@
 Prologue outputs (INT8 Q/K codes and scales, E4M3 V codes and scales, k_mean)
 must match bit for bit. The attention output must satisfy, against the oracle
 on the same inputs, max|O - O_oracle| <= 1e-2 max|O_oracle| and cosine >=
-0.9995, and against fp64 exact attention cosine >= 0.999 wherever the method
-itself (the oracle) reaches it; where the oracle does not (a property of the
-per-block INT8 K quantization on those inputs), the GPU must not fall more
-than 2e-4 below the oracle's own cosine.
+0.9995, and against fp64 exact attention cosine >= 0.999. Three named input
+classes miss that last criterion with the oracle exactly as with the GPU, so
+it is a property of the method there (METHOD_LIMITED below): for them the
+GPU must not fall more than 2e-4 below the oracle's own cosine, the oracle
+must indeed be below 0.999 (else the exception is stale), and the case is
+recorded as a missed criterion.
 """
 import json
 import math
@@ -24,6 +26,16 @@ MAXABS_TOL = 1e-2
 COS_ORACLE = 0.9995
 COS_EXACT = 0.999
 RESULTS = []
+# Input classes on which the method itself (the oracle) stays below cosine
+# 0.999 against fp64 exact attention, with the reason.
+METHOD_LIMITED = {
+    "C5": "1 % of K entries are N(0, 20^2) outliers, so per-32-row INT8 blocks quantize the ordinary keys "
+          "to 2-3 levels",
+    "qscale256": "Q scaled by 2^8: scores of hundreds of log2 units, rows close to one-hot, where the FP8 "
+                 "rounding of the few non-negligible probabilities dominates",
+    "causal_C3": "C3's per-head Q and K scales up to 3 make rows peaky (its non-causal rows reach only 0.99902); "
+                 "causal rows, averaging fewer keys, fall just below",
+}
 
 
 @pytest.fixture(scope="module")
@@ -131,6 +143,86 @@ def test_prologue_is_deterministic(sage):
         assert np.array_equal(a[key], b[key]), key
 
 
+def _scaled(bits, factor):
+    """BF16 bits times a power of two, rounded back to BF16 by torch (values
+    pushed among the BF16 subnormals lose low bits; both sides see the result)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).float() * factor
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("smooth_k", [False, True])
+def test_tiny_blocks_and_channels(sage, D, smooth_k):
+    """Blocks and channels whose absmax a makes 127/a or 448/a overflow a float
+    (a below about 3.7e-37 and 1.3e-36; BF16 subnormals reach 9.2e-41): the
+    prologue lifts them by 2^64 exactly as the oracle does, bit for bit; the
+    output is finite and within tolerance of the oracle. A V channel of +-0
+    only has scale 0 and codes 0 (its negative zeros too)."""
+    import torch
+    B, S, H = 2, 300, 3
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=8100 + D + int(smooth_k))
+    q, k, v = (x.copy() for x in inputs(w))
+    q[0, 32:64, 0] = _scaled(q[0, 32:64, 0], 2.0 ** -124)        # one tiny Q block
+    q[1, :, 1] = _scaled(q[1, :, 1], 2.0 ** -130)                # a whole head of tiny Q (scores vanish)
+    k[0, 64:96, 1] = _scaled(k[0, 64:96, 1], 2.0 ** -126)        # a tiny K block (smooth_k off)
+    k[1, :, 2] = _scaled(k[1, :, 2], 2.0 ** -125)                # a tiny K head: K - mean stays tiny
+    v[0, :, 0, 5] = _scaled(v[0, :, 0, 5], 2.0 ** -122)          # V channel with 448/a overflowing
+    v[1, :, 2, 9] = _scaled(v[1, :, 2, 9], 2.0 ** -60)           # lifted, quotient finite either way
+    v[0, :, 1, 3] = _scaled(v[0, :, 1, 3], 2.0 ** -140)          # all +-0: a zero channel with negative zeros
+    v[0, :, 1, 4] = _scaled(v[0, :, 1, 4], 2.0 ** -128)          # BF16 subnormals with few bits
+    o = oracle.prepare(q, k, v, smooth_k)
+    assert o["q_scale"][0, 0, 1] < 3.7e-37 and o["v_scale"][0, 0, 5] < 1.3e-36 / 448
+    assert o["v_scale"][0, 1, 3] == 0 and np.any(v[0, :, 1, 3] == 0x8000) and o["v_scale"][0, 1, 4] > 0
+    g = gpu_prepare(sage, q, k, v, smooth_k)
+    check_prologue(g, o, S, smooth_k=smooth_k)
+    out = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, False, smooth_k)
+    torch.cuda.synchronize()
+    O = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(O)))
+    compare_attention(f"tiny_{D}_{'sk' if smooth_k else 'nosk'}", O, oracle.attn(o, w.sm_scale),
+                      oracle.exact(q, k, v, w.sm_scale))
+
+
+def _adversarial_keys(k, rng):
+    """Key channels whose fp64 running sums are not exact: 2^60, 1, -2^60, ...;
+    2^70 and 2^-70 of both signs; subnormals beside 2^100; one channel of random
+    exponents over the whole BF16 range."""
+    import torch
+    B, S, H, D = k.shape
+    f = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).float()
+    s = torch.arange(S)
+    f[:, :, :, 0] = torch.tensor([2.0 ** 60, 1.0, -(2.0 ** 60)])[s % 3][None, :, None]
+    f[:, :, :, 1] = (torch.where(s % 2 == 0, 2.0 ** 70, 2.0 ** -70) * torch.where(s % 4 < 2, 1.0, -1.0))[None, :, None]
+    f[:, :, :, 2] = torch.where(s % 7 == 0, 2.0 ** 100, 2.0 ** -130)[None, :, None]
+    e = torch.from_numpy(rng.integers(-130, 110, (B, S, H))).float()
+    f[:, :, :, 3] = torch.from_numpy(rng.standard_normal((B, S, H))).float() * torch.pow(2.0, e)
+    return f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("B,S,H,D", [(1, 300, 2, 128), (2, 20000, 2, 128), (1, 4097, 3, 64)])
+def test_k_mean_exact_on_adversarial_channels(sage, B, S, H, D):
+    """smooth_k on key channels whose fp64 sums depend on the order of
+    addition: the GPU's checked fp64 sums fall back to exact integer sums and
+    k_mean (and with it every K code) matches the oracle's correctly rounded
+    mean bit for bit. The attention output (rows made near one-hot by keys of
+    magnitude 2^60 and more) is compared with the oracle only."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=True, base_seed=8200 + S)
+    q, k, v = inputs(w)
+    k = _adversarial_keys(k, np.random.default_rng(S))
+    o = oracle.prepare(q, k, v, True)
+    kd = synth.bf16_to_float(k[0, :, 0, 0]).astype(np.float64)
+    assert o["k_mean"][0, 0, 0] == np.float32(math.fsum(kd.tolist()) / S)
+    g = gpu_prepare(sage, q, k, v, True)
+    check_prologue(g, o, S)
+    if S <= 4097:
+        out = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", False, w.sm_scale, False, True)
+        torch.cuda.synchronize()
+        compare_attention(f"adversarial_kmean_{B}x{S}x{H}x{D}", out.view(torch.int16).cpu().numpy().view(np.uint16),
+                          oracle.attn(o, w.sm_scale), None)
+
+
 # ------------------------------------------------------------------ attention
 def run_sageattn(sage, q, k, v, smooth_k, sm_scale):
     import torch
@@ -139,17 +231,30 @@ def run_sageattn(sage, q, k, v, smooth_k, sm_scale):
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def compare_attention(name, O_gpu_bits, O_orc_bits, E):
+def compare_attention(name, O_gpu_bits, O_orc_bits, E, limited=None):
+    """limited: a key of METHOD_LIMITED for the input classes where the method
+    itself misses cosine 0.999 against exact attention; E None: no exact
+    reference for this case (only the oracle bounds apply)."""
     G = oracle.bf16_bits_to_f64(O_gpu_bits)
     R = oracle.bf16_bits_to_f64(O_orc_bits)
     rec = dict(case=name, maxabs_vs_oracle=oracle.max_abs_rel(G, R), cos_vs_oracle=oracle.cosine(G, R),
-               cos_vs_exact=oracle.cosine(G, E), oracle_cos_vs_exact=oracle.cosine(R, E),
-               maxabs_vs_exact=oracle.max_abs_rel(G, E), bits_equal_frac=float(np.mean(O_gpu_bits == O_orc_bits)))
+               bits_equal_frac=float(np.mean(O_gpu_bits == O_orc_bits)))
+    if E is not None:
+        rec.update(cos_vs_exact=oracle.cosine(G, E), oracle_cos_vs_exact=oracle.cosine(R, E),
+                   maxabs_vs_exact=oracle.max_abs_rel(G, E))
+        if limited is not None:
+            rec["criterion_missed"] = f"cosine vs exact {rec['cos_vs_exact']:.5f} < {COS_EXACT}: {METHOD_LIMITED[limited]}"
     RESULTS.append(rec)
     print(json.dumps(rec))
     assert rec["maxabs_vs_oracle"] <= MAXABS_TOL, rec
     assert rec["cos_vs_oracle"] >= COS_ORACLE, rec
-    assert rec["cos_vs_exact"] >= min(COS_EXACT, rec["oracle_cos_vs_exact"] - 2e-4), rec
+    if E is None:
+        return
+    if limited is None:
+        assert rec["cos_vs_exact"] >= COS_EXACT, rec
+    else:
+        assert rec["oracle_cos_vs_exact"] < COS_EXACT, ("stale exception", limited, rec)
+        assert rec["cos_vs_exact"] >= rec["oracle_cos_vs_exact"] - 2e-4, rec
 
 
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
@@ -181,7 +286,7 @@ def test_attention_workload(sage, name):
         return
     E = oracle.exact(q, k, v, w.sm_scale, rows=rows)
     G = O if rows is None else O[rows[:, 0], rows[:, 2], rows[:, 1]]
-    compare_attention(name, G, R, E)
+    compare_attention(name, G, R, E, limited="C5" if name == "C5" else None)
 
 
 @pytest.mark.parametrize("B,S,H,smooth_k", [(1, 1, 1, False), (2, 33, 3, True), (1, 129, 2, False),
@@ -332,7 +437,37 @@ def test_extreme_score_scales_keep_masked_keys_out(sage, qscale, B, S, H, D, cau
     R, lse_o = oracle.attn(oracle.prepare(q, k, v, True), w.sm_scale, want_lse=True, causal=causal)
     E = oracle.exact(q, k, v, w.sm_scale, causal=causal)
     name = f"qscale{qscale:g}_{B}x{S}x{H}x{D}{'_causal' if causal else ''}"
-    compare_attention(name, out.view(torch.int16).cpu().numpy().view(np.uint16), R, E)
+    compare_attention(name, out.view(torch.int16).cpu().numpy().view(np.uint16), R, E,
+                      limited="qscale256" if qscale == 2.0 ** 8 else None)
+    check_lse("lse_" + name, lse.cpu().numpy(), lse_o)
+
+
+@pytest.mark.parametrize("B,S,H,D,causal,smooth_k", [(1, 700, 3, 128, False, False), (2, 333, 3, 128, True, True),
+                                                      (1, 1000, 3, 64, True, False), (1, 300, 3, 64, False, True)])
+def test_large_scores_take_the_exact_softmax_form(sage, B, S, H, D, causal, smooth_k):
+    """Scores of 2^19 and more (log2 units), where the kernel's one-FMA
+    exponent would no longer round the score first as the method does (and
+    could exceed the FP8 range): the waves that may meet scores of 2^14 run the
+    method's exact form. Head 0: Q and K times 2^8 (every wave exact); head 1:
+    the queries of one wave times 2^10 (that wave exact, the other three of its
+    workgroup fast, so the two loop copies run side by side); head 2: one
+    32-key block times 2^12 (every wave exact). Output and log-sum-exp against
+    the oracle; the rows are near one-hot, so exact attention is not compared."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=6300 + S + D)
+    q, k, v = (x.copy() for x in inputs(w))
+    q[:, :, 0] = _scaled(q[:, :, 0], 2.0 ** 8)
+    k[:, :, 0] = _scaled(k[:, :, 0], 2.0 ** 8)
+    q[:, 32:64, 1] = _scaled(q[:, 32:64, 1], 2.0 ** 10)
+    k[:, 128:160, 2] = _scaled(k[:, 128:160, 2], 2.0 ** 12)
+    o = oracle.prepare(q, k, v, smooth_k)
+    out, lse = sage.sageattn(to_dev(q), to_dev(k), to_dev(v), "NHD", causal, w.sm_scale, True, smooth_k)
+    torch.cuda.synchronize()
+    O = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(O)))
+    R, lse_o = oracle.attn(o, w.sm_scale, want_lse=True, causal=causal)
+    name = f"large_scores_{B}x{S}x{H}x{D}{'_causal' if causal else ''}"
+    compare_attention(name, O, R, None)
     check_lse("lse_" + name, lse.cpu().numpy(), lse_o)
 
 
@@ -374,7 +509,8 @@ def test_causal_workload_rows(sage, name, n):
     R, lse_o = oracle.attn(prep, w.sm_scale, rows=rows, want_lse=True, causal=True)
     E = oracle.exact(q, k, v, w.sm_scale, rows=rows, causal=True)
     O = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    compare_attention(f"causal_{name}", O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E)
+    compare_attention(f"causal_{name}", O[rows[:, 0], rows[:, 2], rows[:, 1]], R, E,
+                      limited="causal_C3" if name == "C3" else None)
     check_lse(f"causal_lse_{name}", lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]], lse_o)
 
 
@@ -627,6 +763,31 @@ def test_calls_on_two_streams_at_once_match_serial_results(sage):
         torch.cuda.synchronize()
         for i in range(4):
             assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), (rep, i)
+
+
+def test_call_on_another_stream_keeps_its_workspace_from_the_current_stream(sage):
+    """A fused call on a side stream without a workspace: the temporary the
+    binding allocates must not be handed to the current stream's allocations
+    while the side stream still works on it. The current stream fills fresh
+    buffers of the workspace's size right after the call; the result is that
+    of a call on the current stream."""
+    import torch
+    w = synth.custom(2, 3000, 6, smooth_k=True, base_seed=6450)
+    q, k, v = (to_dev(x) for x in inputs(w))
+    ref = sage.sageattn(q, k, v, sm_scale=0.1)
+    torch.cuda.synchronize()
+    nws = sage.fused_workspace_bytes(w.B, w.S, w.H, w.D)
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            out = torch.empty_like(q)
+        out2 = sage.sageattn(q, k, v, sm_scale=0.1, out=out, stream=side)
+        junk = [torch.full((nws,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(3)]
+        torch.cuda.synchronize()
+        assert out2 is out
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        del junk
 
 
 def test_outputs_leave_guard_bands_untouched(sage):

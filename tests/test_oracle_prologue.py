@@ -182,6 +182,11 @@ def test_zero_channel_and_zero_head():
     out = oracle.prepare_head(z, z, z, smooth_k=True)
     assert not out["q8"].any() and not out["k8"].any() and not out["v8t"].any()
     assert not out["q_scale"].any() and not out["k_scale"].any() and not out["v_scale"].any()
+    # negative zeros are zeros: a block or channel of +-0 has scale 0 and codes 0
+    nz = z.copy()
+    nz[::3] = 0x8000
+    out = oracle.prepare_head(nz, nz, nz, smooth_k=False)
+    assert not out["q8"].any() and not out["k8"].any() and not out["v8t"].any() and not out["v_scale"].any()
 
 
 def test_full_tensor_prepare_matches_per_head():
