@@ -123,6 +123,22 @@ sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_
                          float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation): sage_prepare
+ * without the workspace argument. The prologue's statistics go to a static
+ * device buffer of SAGE_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds
+ * on each GPU it runs on until the process ends; the call allocates and frees
+ * nothing. Same arguments (minus ws, ws_bytes), outputs, validation order and
+ * results as sage_prepare; a problem whose sage_prepare_workspace_bytes()
+ * exceeds the buffer returns SAGE_ERR_WORKSPACE_TOO_SMALL before any device
+ * call. Every call on one GPU uses the same buffer, which keeps the last
+ * call's contents (no call relies on them): calls that overlap on one GPU (two
+ * streams, or unordered host threads) race and give undefined results. */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+sage_status sage_prepare_noalloc(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k,
+                                 int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale,
+                                 float* k_mean, void* stream);
+
 /* The attention step (issue, "The kernel") on sage_prepare's outputs:
  *   t_ij = float(q8_i . k8_j) * ((q_scale[i/32] * k_scale[j/32]) * (sm_scale * log2 e))
  *   online softmax in FP32 over key tiles of sage_kv_tile() keys in ascending

@@ -83,6 +83,8 @@ def lib():
         L.sage_fused_workspace_bytes.restype = ctypes.c_size_t
         L.sage_prepare.argtypes = [_T, _T, _T, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.sage_prepare.restype = ctypes.c_int
+        L.sage_prepare_noalloc.argtypes = [_T, _T, _T, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.sage_prepare_noalloc.restype = ctypes.c_int
         L.sage_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P]
         L.sage_attn.restype = ctypes.c_int
         L.sage_attn_lse.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _T, _P, _P]

@@ -170,6 +170,41 @@ size_t fused_bytes(int64_t B, int64_t S, int64_t H, int64_t D, FusedWs* carve, v
   return 3 * tens + 2 * sc + vs + pro;
 }
 
+// ---- the prologue without a workspace argument
+// Static scratch for the prologue's statistics (per-chunk key sums and V
+// maxima, per-channel constants), for callers that cannot allocate. Each GPU
+// the library runs on holds its own copy until the process ends. In host code
+// the name `scratch` is only a stand-in: the device address of each GPU's copy
+// comes from hipGetSymbolAddress, once per device with that device current,
+// and only that address is passed to kernels.
+constexpr size_t kScratchBytes = SAGE_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or null (with the error set).
+void* scratch_of_current_device(sage_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = fail(SAGE_ERR_DEVICE, "no usable current device for the static scratch (%d)", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *st = fail(SAGE_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 sage_status prepare_impl(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k, int8_t* q8,
                          float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale, float* k_mean,
                          void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -223,6 +258,34 @@ sage_status sage_prepare(const sage_tensor* q, const sage_tensor* k, const sage_
   if (empty) return ok();
   if ((s = check_device())) return s;
   return prepare_impl(q, k, v, smooth_k, q8, q_scale, k8, k_scale, v8t, v_scale, k_mean, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_prepare_noalloc(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, int smooth_k,
+                                 int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, uint8_t* v8t, float* v_scale,
+                                 float* k_mean, void* stream) {
+  sage_status s;
+  if ((s = check_tensor_args(q, "q")) || (s = check_tensor_args(k, "k")) || (s = check_tensor_args(v, "v"))) return s;
+  const int64_t B = q->size[0], S = q->size[1], H = q->size[2];
+  const bool empty = B == 0 || S == 0 || H == 0;
+  if (!empty && (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale))
+    return fail(SAGE_ERR_INVALID_ARGUMENT, "null output pointer");
+  if ((s = check_tensor_contract(q, "q", nullptr)) || (s = check_tensor_contract(k, "k", q->size)) ||
+      (s = check_tensor_contract(v, "v", q->size)) || (s = check_extent(B, S, H)))
+    return s;
+  const void* outs[] = {q8, q_scale, k8, k_scale, v8t, v_scale, k_mean};
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return fail(SAGE_ERR_UNSUPPORTED, "output pointer not 16-byte aligned");
+  const size_t need = sage_prepare_workspace_bytes(B, S, H, q->size[3], smooth_k);
+  if (need > kScratchBytes)
+    return fail(SAGE_ERR_WORKSPACE_TOO_SMALL,
+                "problem needs %zu bytes of scratch; the static scratch of the allocation-free prologue holds %zu",
+                need, kScratchBytes);
+  if (empty) return ok();
+  if ((s = check_device())) return s;
+  void* ws = scratch_of_current_device(&s);
+  if (!ws) return s;
+  return prepare_impl(q, k, v, smooth_k, q8, q_scale, k8, k_scale, v8t, v_scale, k_mean, ws, kScratchBytes,
                       static_cast<hipStream_t>(stream));
 }
 

@@ -284,3 +284,24 @@ def test_binding_refuses_host_tensors_before_any_library_call():
     prep = {key: torch.zeros(4) for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale")}
     with pytest.raises(ValueError, match="GPU"):
         sage.attn(prep, 0.1)
+
+
+def test_prepare_noalloc_validates_and_rejects_problems_beyond_its_scratch():
+    """The allocation-free prologue checks its arguments like sage_prepare and
+    refuses a problem whose statistics do not fit its static scratch, all
+    before any device call."""
+    h = Host()
+    L = sage.lib()
+    outs = [h.buf() for _ in range(7)]
+    q, k, v = h.tensor(), h.tensor(), h.tensor()
+    assert L.sage_prepare_noalloc(None, ctypes.byref(k), ctypes.byref(v), 1, *outs, None) == INVALID
+    assert L.sage_prepare_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1, None, *outs[1:], None) == INVALID
+    bad = h.tensor(dtype=2)
+    assert L.sage_prepare_noalloc(ctypes.byref(q), ctypes.byref(bad), ctypes.byref(v), 1, *outs, None) == UNSUPPORTED
+    big = (512, 4096, 32, 128)
+    assert L.sage_prepare_workspace_bytes(*big, 1) > (16 << 20)
+    qb, kb, vb = h.tensor(size=big), h.tensor(size=big), h.tensor(size=big)
+    assert L.sage_prepare_noalloc(ctypes.byref(qb), ctypes.byref(kb), ctypes.byref(vb), 1, *outs, None) == WS_SMALL
+    assert "static scratch" in L.sage_last_error().decode()
+    empty = h.tensor(size=(0, 64, 2, 128))
+    assert L.sage_prepare_noalloc(ctypes.byref(empty), ctypes.byref(empty), ctypes.byref(empty), 1, *outs, None) == OK
