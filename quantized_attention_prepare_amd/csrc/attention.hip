@@ -215,7 +215,7 @@ SAGE_INLINE float block_max(const v16i& x, float c) {
 // exceed 448 (an FP8 NaN). Waves whose scores may reach 2^14 in magnitude
 // therefore take the exact form (kExact true, moff = m'): the method's own
 // steps, p = exp2(t - m') with t rounded to float first, then 448 p.
-template <bool kExact>
+template <bool kExact, bool kFirst = false>
 SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v8i (&pk)[2], float (&ps)[4]) {
   float p[4];
 #pragma unroll
@@ -224,7 +224,10 @@ SAGE_INLINE void exp_group(const v16i& sc, int kb, int g, float c, float moff, v
       p[u] = 448.0f * __builtin_amdgcn_exp2f((float)sc[4 * g + u] * c - moff);
     else
       p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[4 * g + u], c, -moff));
-    ps[u] += p[u];
+    if constexpr (kFirst)   // the tile's first group starts the partial sums (0 + p would cost an add)
+      ps[u] = p[u];
+    else
+      ps[u] += p[u];
   }
   const int j = 16 * (kb & 1) + 4 * g;   // k-slot of p[0] within the 64-key half-tile
   // the first conversion writes bytes 0-1 and the second bytes 2-3, so the word
@@ -324,8 +327,8 @@ SAGE_INLINE void tile_iteration(WaveState<D>& st, v16i (&sc)[4], v16i (&snext)[4
     SAGE_FENCE();                                                                                             \
   }
   float m_new, alpha, moff;
-  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#define SAGE_EXP(KB_, G_) exp_group<kExact>(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
+  float ps[4];
+#define SAGE_EXP(KB_, G_) exp_group<kExact, (KB_) == 0 && (G_) == 0>(sc[KB_], KB_, G_, cblk[KB_], moff, st.pk, ps)
 #define SAGE_L_UPDATE()                                                                               \
   {                                                                                                   \
     float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                   \
@@ -451,6 +454,11 @@ SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buff
                           const float* __restrict__ v_scale, const Bf16OutView& o, float* __restrict__ lse) {
   using Dm = Dim<D>;
   constexpr int TB = Dm::kTileBytes;
+  // q_scale * (sm_scale * log2 e): the fast form's block constant is this times
+  // k_scale, one product per block (an ulp away from the method's
+  // (q_scale * k_scale) * (sm_scale * log2 e), well inside the fast form's
+  // other differences)
+  const float qsl2 = qs * sl2;
 #define KBUF(i) (lds + (i) * TB)
 #define VBUF(i) (lds + (2 + (i)) * TB)
   WaveState<D> st;
@@ -487,8 +495,12 @@ SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buff
     const bool diag = kCausal && t_ == ntw - 1;                                                              \
     const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                           \
     const float kss[4] = {ksv.x, ksv.y, ksv.z, ksv.w};                                                       \
-    float cblk[4]; /* (q_scale * k_scale) * sm_scale * log2 e; +inf for a block masked for the whole wave */ \
-    for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : (qs * kss[kb]) * sl2;             \
+    /* q_scale * k_scale * sm_scale * log2 e (the exact form: the method's product order); */                \
+    /* +inf for a block masked for the whole wave, which only masked tiles have */                           \
+    float cblk[4];                                                                                           \
+    for (int kb = 0; kb < 4; ++kb) cblk[kb] = kExact ? (qs * kss[kb]) * sl2 : qsl2 * kss[kb];                \
+    if (diag || nvalid < kKvTile)                                                                            \
+      for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : cblk[kb];                       \
     if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                             \
     tile_iteration<D, HAS_PREV_, kExact>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                    \
                                          diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1), \
