@@ -114,6 +114,17 @@ def test_prologue_bit_exact_ragged(sage, B, S, H, smooth_k):
     check_prologue(gpu_prepare(sage, q, k, v, smooth_k), oracle.prepare(q, k, v, smooth_k), S)
 
 
+@pytest.mark.parametrize("B,S,H,D", [(1, 512, 3, 128), (2, 385, 2, 64), (1, 128, 4, 128), (3, 129, 2, 64),
+                                     (1, 513, 2, 128), (2, 512, 2, 64)])
+@pytest.mark.parametrize("smooth_k", [False, True])
+def test_prologue_bit_exact_short_heads(sage, B, S, H, D, smooth_k):
+    """Short heads (one to five 128-row chunks, full and ragged), both head
+    dims: few statistics partials per head, a single chunk per head."""
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=8300 + S + D)
+    q, k, v = inputs(w)
+    check_prologue(gpu_prepare(sage, q, k, v, smooth_k), oracle.prepare(q, k, v, smooth_k), S)
+
+
 def test_e4m3_conversion_of_every_in_range_bf16(sage):
     # channel 0 of V holds every BF16 value of magnitude <= 448 (both signs) and
     # the value 448 itself, so its scale is exactly 1 and the codes are
