@@ -44,10 +44,10 @@ def prologue_compulsory_bytes(w) -> int:
 
 def kernel_source_hash(main: str = "attention.hip") -> str:
     """First 16 hex digits of sha256 over the code of a kernel source and the shared
-    internal header, with comments removed and every run of whitespace made one space:
-    a comment edit or a re-indent keeps the hash."""
+    headers it includes, with comments removed and every run of whitespace made one
+    space: a comment edit or a re-indent keeps the hash."""
     h = hashlib.sha256()
-    for f in (main, "sage_internal.hpp"):
+    for f in (main, "sage_internal.hpp", "prologue_ops.hpp"):
         with open(os.path.join(ROOT, "quantized_attention_prepare_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)

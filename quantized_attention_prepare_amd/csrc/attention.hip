@@ -50,7 +50,7 @@
 // f(r) = (r>>1)&7, for K, whose rows are read in the permuted order pi,
 // f(r) = ((r>>1)&3) | ((r>>4)&1)<<2. 64-byte rows (four per bank row; K and Q
 // at D = 64): for Q f(r) = (r>>2)&3, for K f(r) = ((r>>2)&1) | ((r>>4)&1)<<1.
-#include "sage_internal.hpp"
+#include "prologue_ops.hpp"
 
 namespace sage {
 namespace {
@@ -445,8 +445,12 @@ SAGE_INLINE void pv_tile(WaveState<D>& st, const uint8_t* vbuf, int half, int co
 // The key loop of one wave, its tail and the epilogue: the online softmax
 // state starts here, so the two copies (fast and exact form) share no state
 // and are register-allocated independently.
-template <int D, bool kCausal, bool kExact>
-SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+// kResident: every K tile of the head is in LDS from lds on (tile t at
+// lds + t TB) and every V tile from vres on, in the layout the copies give
+// them; the loop then copies nothing and passes no barrier, so the waves of a
+// workgroup may run different numbers of tiles.
+template <int D, bool kCausal, bool kExact, bool kResident = false>
+SAGE_INLINE void key_loop(uint8_t* lds, uint8_t* vres, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                           const uint32_t (&k_lane_off)[Dim<D>::kCopyInstr],
                           const uint32_t (&v_lane_off)[Dim<D>::kCopyInstr], const float* ks, float qs, float sl2,
                           const uint8_t* qrow, int prow, int wave, int half, int col, int ntw, int ntiles,
@@ -487,10 +491,12 @@ SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buff
 #define SAGE_ITERATION(T_, PAR_, HAS_PREV_, CUR_, NEXT_)                                                     \
   {                                                                                                          \
     const int t_ = (T_);                                                                                     \
-    __builtin_amdgcn_s_waitcnt(0);   /* this wave's copies have landed */                                    \
-    __syncthreads();                 /* ... everyone's; K(t) and V(t-2) are no longer read */                \
-    if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                   \
-    load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                                 \
+    if constexpr (!kResident) {                                                                              \
+      __builtin_amdgcn_s_waitcnt(0); /* this wave's copies have landed */                                    \
+      __syncthreads();               /* ... everyone's; K(t) and V(t-2) are no longer read */                \
+      if (t_ + 2 < ntw) load_k<D>(KBUF(PAR_), rk, t_ + 2, k_lane_off, wave);                                 \
+      load_v<D>(VBUF(PAR_), rv, t_, spad32, v_lane_off, wave);                                               \
+    }                                                                                                        \
     const int nvalid = t_ == ntiles - 1 ? last_valid : kKvTile;                                              \
     const bool diag = kCausal && t_ == ntw - 1;                                                              \
     const int nblk = diag ? min(32 * (wave + 1), nvalid) : nvalid;                                           \
@@ -503,8 +509,10 @@ SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buff
       for (int kb = 0; kb < 4; ++kb) cblk[kb] = 32 * kb >= nblk ? INFINITY : cblk[kb];                       \
     if (t_ + 1 < ntw) ksv = *reinterpret_cast<const float4*>(ks + 4 * (t_ + 1));                             \
     tile_iteration<D, HAS_PREV_, kExact>(st, CUR_, NEXT_, cblk, diag || nvalid < kKvTile,                    \
-                                         diag ? min(32 * wave + col + 1, nvalid) : nvalid, VBUF((PAR_) ^ 1), \
-                                         KBUF((PAR_) ^ 1), qrow, half, col, prow);                           \
+                                         diag ? min(32 * wave + col + 1, nvalid) : nvalid,                   \
+                                         kResident ? vres + (t_ - 1) * TB : VBUF((PAR_) ^ 1),                \
+                                         kResident ? lds + (t_ + 1) * TB : KBUF((PAR_) ^ 1), qrow, half, col, \
+                                         prow);                                                              \
   }
   // tile t uses buffer pair t & 1; the parity is spelled out so that buffer
   // addresses fold into the LDS instructions' offsets (t is odd in the loop)
@@ -532,9 +540,11 @@ SAGE_INLINE void key_loop(uint8_t* lds, __amdgpu_buffer_rsrc_t rk, __amdgpu_buff
       }
   }
   // PV of the last tile
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  pv_tile<D>(st, VBUF((ntw - 1) & 1), half, col);
+  if constexpr (!kResident) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  pv_tile<D>(st, kResident ? vres + (ntw - 1) * TB : VBUF((ntw - 1) & 1), half, col);
 
   // ---- epilogue: O = o * v_scale / (448 l)
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
@@ -674,16 +684,318 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (__builtin_expect(__builtin_amdgcn_readfirstlane(kmax) >= kexact, 0)) {
-    key_loop<D, kCausal, true>(lds, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
+    key_loop<D, kCausal, true>(lds, nullptr, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
                                ntiles, last_valid, spad32, q0, S, bh, b, h, v_scale, o, lse);
     return;
   }
-  key_loop<D, kCausal, false>(lds, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
+  key_loop<D, kCausal, false>(lds, nullptr, rk, rv, k_lane_off, v_lane_off, ks, qs, sl2, qrow, prow, wave, half, col, ntw,
                               ntiles, last_valid, spad32, q0, S, bh, b, h, v_scale, o, lse);
 #undef KBUF
 #undef VBUF
 }
 
+
+// ------------------------------------------------------------- short heads
+// A head of at most Short<D>::kTiles key tiles is handled start to end by one
+// workgroup of kShortWaves waves, in one launch: first the prologue's steps for
+// the head, with the arithmetic of its three passes (the same codes and
+// scales), the Q codes and all scales going to the workspace and the K and V
+// codes straight into LDS, in the layout the tile copies above give them; then
+// each wave runs the key loop over those resident tiles for its 32-query
+// blocks. Wave w takes the 32-row blocks w, w + 8, ... in both phases.
+constexpr int kShortWaves = 8;
+template <int D>
+struct Short {
+  static constexpr int kTiles = D == 128 ? 3 : 8;   // resident K and V tiles that fit in LDS
+};
+
+// Codes of rows 32 (j % 4) + G i + g of K tile j / 4 (channels 8c..8c+7 in
+// lo[i], hi[i]) into the resident tile: chunk (c / 2) of row r sits at slot
+// (c / 2) XOR fk(r).
+template <int D>
+SAGE_INLINE void put_k_rows(uint8_t* kres, int j, const uint32_t (&lo)[Geo<D>::I], const uint32_t (&hi)[Geo<D>::I],
+                            int c, int g) {
+  using Gm = Geo<D>;
+  uint8_t* tile = kres + (j >> 2) * Dim<D>::kTileBytes;
+#pragma unroll
+  for (int i = 0; i < Gm::I; ++i) {
+    const int r = 32 * (j & 3) + Gm::G * i + g;
+    *reinterpret_cast<uint2*>(tile + r * D + ((((c >> 1) ^ Dim<D>::fk(r)) << 4) | ((c & 1) << 3))) =
+        make_uint2(lo[i], hi[i]);
+  }
+}
+
+template <int D, bool kCausal>
+__global__ void __launch_bounds__(64 * kShortWaves, 1)
+short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int smooth_k, float sl2,
+             int8_t* __restrict__ q8, float* __restrict__ q_scale, float* __restrict__ k_scale,
+             float* __restrict__ v_scale, Bf16OutView o, float* __restrict__ lse) {
+  using Gm = Geo<D>;
+  using Dm = Dim<D>;
+  constexpr int TB = Dm::kTileBytes, NT = Short<D>::kTiles, NW = kShortWaves;
+  // [K tiles][V tiles][32 query rows per wave]; during the prologue steps the
+  // per-wave channel statistics and the exact-sum digits overlay the V tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NT * TB + NW * 32 * D];
+  __shared__ float s_kmean[D], s_vinv[D], s_vlift[D];
+  static_assert(NW * D * (sizeof(double) + sizeof(float)) <= NT * TB, "statistics overlay");
+  static_assert(kExactSlices * kDigits * D * sizeof(long long) <= NT * TB, "digit overlay");
+  uint8_t* const kres = lds;
+  uint8_t* const vres = lds + NT * TB;
+  double(*const fsum)[D] = reinterpret_cast<double(*)[D]>(vres);
+  float(*const fmx)[D] = reinterpret_cast<float(*)[D]>(vres + NW * D * sizeof(double));
+  long long(*const dig)[kDigits][D] = reinterpret_cast<long long(*)[kDigits][D]>(vres);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int nt = (int)(S_pad / kKvTile), nb = 4 * nt;   // key tiles, 32-row blocks
+  const int c = lane % Gm::L, g = lane / Gm::L;
+  const uint16_t* qb = q.data + b * q.sb + h * q.sh + 8 * c;
+  const uint16_t* kb = k.data + b * k.sb + h * k.sh + 8 * c;
+  const uint16_t* vb = v.data + b * v.sb + h * v.sh + 8 * c;
+
+  // ---- Q codes, K codes when smooth_k is off, channel statistics
+  double ksum[8];
+  float vmax[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ksum[e] = 0.0; vmax[e] = 0.0f; }
+  for (int j = w; j < nb; j += NW) {
+    const int64_t r0 = 32 * (int64_t)j;
+    float x[8 * Gm::I];
+#pragma unroll
+    for (int i = 0; i < Gm::I; ++i) {
+      const int64_t row = r0 + Gm::G * i + g;
+      Row16 r = row < S ? load16nt(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
+      unpack(r, &x[i * 8]);
+    }
+    quant_block_store<D>(x, q8 + (bh * S_pad + r0) * D, q_scale + bh * nb + j, lane);
+#pragma unroll
+    for (int i = 0; i < Gm::I; ++i) {
+      const int64_t row = r0 + Gm::G * i + g;
+      Row16 r = row < S ? load16(kb + row * k.ss) : Row16{{0, 0, 0, 0}};
+      unpack(r, &x[i * 8]);
+    }
+    if (smooth_k) {
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ksum[e] = add_exact_or_nan(ksum[e], (double)x[i * 8 + e]);
+    } else {
+      uint32_t lo[Gm::I], hi[Gm::I];
+      const float sc = quant_block_codes<D>(x, lo, hi);
+      if (lane == 0) k_scale[bh * nb + j] = sc;
+      put_k_rows<D>(kres, j, lo, hi, c, g);
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::I; ++i) {
+      const int64_t row = r0 + Gm::G * i + g;
+      Row16 r = row < S ? load16(vb + row * v.ss) : Row16{{0, 0, 0, 0}};
+      float y[8];
+      unpack(r, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vmax[e] = fmaxf(vmax[e], fabsf(y[e]));
+    }
+  }
+  // the wave's statistics, folded over the lanes of a channel, then over the
+  // waves in order (every addition checked, as in the three passes)
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int m = Gm::L; m < 64; m <<= 1) {
+      ksum[e] = add_exact_or_nan(ksum[e], __shfl_xor(ksum[e], m, 64));
+      vmax[e] = fmaxf(vmax[e], __shfl_xor(vmax[e], m, 64));
+    }
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { fsum[w][8 * c + e] = ksum[e]; fmx[w][8 * c + e] = vmax[e]; }
+  }
+  __syncthreads();
+  const int d = tid % D, js = tid / D;
+  double ssum = 0.0;
+  float amax = 0.0f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    ssum = add_exact_or_nan(ssum, fsum[ww][d]);
+    amax = fmaxf(amax, fmx[ww][d]);
+  }
+  // a NaN sum: that channel is summed exactly from K (rare; uniform branch).
+  // The barrier ends every read of the statistics before the digits reuse
+  // their LDS.
+  const bool redo = smooth_k && ssum != ssum;
+  if (__syncthreads_or(redo)) {
+    if (js < kExactSlices) {
+#pragma unroll
+      for (int kk = 0; kk < kDigits; ++kk) dig[js][kk][d] = 0;
+      if (redo) exact_sum_rows(k.data + b * k.sb + h * k.sh + d, k.ss, S, js, &dig[js][0][d], D);
+    }
+    __syncthreads();
+    if (redo) {
+      long long wd[kDigits];
+#pragma unroll
+      for (int kk = 0; kk < kDigits; ++kk) {
+        long long t = 0;
+#pragma unroll
+        for (int i = 0; i < kExactSlices; ++i) t += dig[i][kk][d];
+        wd[kk] = t;
+      }
+      ssum = digits_to_double(wd);
+    }
+  }
+  if (tid < D) {
+    s_kmean[tid] = smooth_k ? (float)(ssum / (double)S) : 0.0f;
+    v_scale[bh * D + tid] = amax == 0.0f ? 0.0f : amax / 448.0f;
+    const float lift = amax < kTiny ? kTinyLift : 1.0f;
+    s_vinv[tid] = amax == 0.0f ? 0.0f : 448.0f / (amax * lift);
+    s_vlift[tid] = lift;
+  }
+  __syncthreads();   // the constants are in place; the overlay is free for the V tiles
+
+  // ---- K codes when smooth_k is on, V codes
+  for (int j = w; j < nb; j += NW) {
+    const int64_t r0 = 32 * (int64_t)j;
+    if (smooth_k) {
+      float km[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) km[e] = s_kmean[8 * c + e];
+      float x[8 * Gm::I];
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i) {
+        const int64_t row = r0 + Gm::G * i + g;
+        float y[8];
+        if (row < S) {
+          unpack(load16(kb + row * k.ss), y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[i * 8 + e] = y[e] - km[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[i * 8 + e] = 0.0f;   // padding rows stay zero
+        }
+      }
+      uint32_t lo[Gm::I], hi[Gm::I];
+      const float sc = quant_block_codes<D>(x, lo, hi);
+      if (lane == 0) k_scale[bh * nb + j] = sc;
+      put_k_rows<D>(kres, j, lo, hi, c, g);
+    }
+    // V: lane (c, g) converts rows 32 (j % 4) + 4 G half + 4 g + u (u = 0..3)
+    // of tile j / 4, channels 8c..8c+7, as the quantize pass does; a channel's
+    // four consecutive keys go to its resident row as one dword, key chunk
+    // (r / 16) at slot (r / 16) XOR ((channel / 2) % 8)
+    float inv[8], lift[8];
+    uint32_t keep[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      inv[e] = s_vinv[8 * c + e];
+      lift[e] = s_vlift[8 * c + e];
+      keep[e] = inv[e] != 0.0f ? 0xFFFFFFFFu : 0u;
+    }
+    bool lifted = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lifted |= lift[e] != 1.0f;
+    lifted = __builtin_amdgcn_ballot_w64(lifted) != 0;
+    uint8_t* vtile = vres + (j >> 2) * TB;
+#pragma unroll
+    for (int half = 0; half < 8 / Gm::G; ++half) {
+      const int rl = 32 * (j & 3) + 4 * Gm::G * half + 4 * g;   // tile row of u = 0
+      uint32_t codes[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) codes[e] = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = r0 + 4 * Gm::G * half + 4 * g + u;
+        float y[8];
+        if (row < S) unpack(load16(vb + row * v.ss), y);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+        }
+        if (lifted) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= lift[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[e] * inv[e], y[e + 1] * inv[e + 1], 0, false);
+          codes[e] |= (pk & 0xFFu) << (8 * u);
+          codes[e + 1] |= ((pk >> 8) & 0xFFu) << (8 * u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = 8 * c + e;
+        *reinterpret_cast<uint32_t*>(vtile + ch * kKvTile + ((((rl >> 4) ^ ((ch >> 1) & 7)) << 4) | (rl & 15))) =
+            codes[e] & keep[e];
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's codes and scales are stored ...
+  __syncthreads();                 // ... and every wave's: the resident tiles are complete
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  // ---- attention, per 32-query block, over the resident tiles
+  const int half = lane >> 5, col = lane & 31;
+  const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+  uint8_t* qlds = lds + 2 * NT * TB + w * 32 * D;
+  const uint8_t* qrow = qlds + col * D;
+  const int last_valid = (int)(S - (int64_t)(nt - 1) * kKvTile);
+  const float* ks = k_scale + bh * nb;
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kBufferWord3);
+  const uint32_t no_off[Dm::kCopyInstr] = {};
+  for (int j = w; j < nb; j += NW) {
+    // the block's query codes (this wave wrote them above) into the wave's rows
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int r = (1024 / D) * i + lane / Dm::kChunks, cc = lane % Dm::kChunks;
+      const uint4 val = *reinterpret_cast<const uint4*>(q8 + (bh * S_pad + 32 * (int64_t)j + r) * D + cc * 16);
+      *reinterpret_cast<uint4*>(qlds + r * D + ((cc ^ Dm::fq(r)) * 16)) = val;
+    }
+    const int wt = j & 3;                        // the block's place in its 128-query tile
+    const int ntw = kCausal ? (j >> 2) + 1 : nt;   // key tiles the block visits
+    float qs = q_scale[bh * nb + j];
+    const uint32_t kexact = __builtin_amdgcn_readfirstlane(__float_as_uint(0x1p-7f / (sl2 * qs)));
+    asm volatile("" : "+v"(qs));
+    uint32_t kmax = 0;
+    for (int i = lane; i < 4 * ntw; i += 64) kmax = max(kmax, __float_as_uint(ks[i]));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(kmax) >= kexact, 0))
+      key_loop<D, kCausal, true, true>(kres, vres, none, none, no_off, no_off, ks, qs, sl2, qrow, prow, wt, half, col,
+                                       ntw, nt, last_valid, (uint32_t)S_pad, 32 * (int64_t)j, S, bh, b, h, v_scale, o,
+                                       lse);
+    else
+      key_loop<D, kCausal, false, true>(kres, vres, none, none, no_off, no_off, ks, qs, sl2, qrow, prow, wt, half,
+                                        col, ntw, nt, last_valid, (uint32_t)S_pad, 32 * (int64_t)j, S, bh, b, h,
+                                        v_scale, o, lse);
+  }
+}
+
+}  // namespace
+
+bool short_fused_fits(int64_t S, int64_t D) {
+  const int64_t nt = padded_len(S) / kKvTile;
+  return nt >= 1 && nt <= (D == 64 ? Short<64>::kTiles : Short<128>::kTiles);
+}
+
+hipError_t launch_fused_short(const Bf16View& q, const Bf16View& k, const Bf16View& v, int64_t B, int64_t S,
+                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, int8_t* q8,
+                              float* q_scale, float* k_scale, float* v_scale, const Bf16OutView& o, float* lse,
+                              hipStream_t stream) {
+  const int64_t S_pad = padded_len(S);
+  const float sl2 = sm_scale * kLog2e;
+#define SAGE_LAUNCH(D_, CAUSAL_)                                                                               \
+  hipLaunchKernelGGL((short_kernel<D_, CAUSAL_>), dim3((unsigned)(B * H)), dim3(64 * kShortWaves), 0, stream, q, k, \
+                     v, H, S, S_pad, smooth_k, sl2, q8, q_scale, k_scale, v_scale, o, lse)
+  if (D == 64) {
+    if (causal) SAGE_LAUNCH(64, true);
+    else SAGE_LAUNCH(64, false);
+  } else {
+    if (causal) SAGE_LAUNCH(128, true);
+    else SAGE_LAUNCH(128, false);
+  }
+#undef SAGE_LAUNCH
+  return hipGetLastError();
+}
+
+namespace {
 }  // namespace
 
 hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,

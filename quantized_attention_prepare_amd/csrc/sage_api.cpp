@@ -364,10 +364,17 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   FusedWs w{};
   fused_bytes(B, S, H, q->size[3], &w, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
+  if (sage::short_fused_fits(S, q->size[3])) {
+    hipError_t e = sage::launch_fused_short(view(q), view(k), view(v), B, S, H, q->size[3], smooth_k ? 1 : 0,
+                                            sm_scale, is_causal != 0, w.q8, w.q_scale, w.k_scale, w.v_scale, ov,
+                                            return_lse ? lse : nullptr, st);
+    if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "fused launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   if ((s = prepare_impl(q, k, v, smooth_k, w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, nullptr, w.prologue,
                         ws_bytes, st)))
     return s;
-  sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
   hipError_t e = sage::launch_attention(w.q8, w.q_scale, w.k8, w.k_scale, w.v8t, w.v_scale, B, S, H, q->size[3],
                                         sm_scale, is_causal != 0, ov, return_lse ? lse : nullptr, st);
   if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));

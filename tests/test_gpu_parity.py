@@ -731,6 +731,26 @@ def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
     assert torch.equal(l3.view(torch.int32), l2.view(torch.int32))
 
 
+@pytest.mark.parametrize("B,S,H,D,causal,smooth_k", [(2, 384, 3, 128, False, True), (1, 300, 2, 128, True, False),
+                                                      (3, 129, 2, 128, False, False), (1, 1, 1, 128, False, True),
+                                                      (2, 1000, 2, 64, True, True), (1, 257, 3, 64, False, False),
+                                                      (2, 385, 2, 128, False, True)])
+def test_fused_short_heads_equal_prepare_then_attn(sage, B, S, H, D, causal, smooth_k):
+    """Heads of up to three key tiles (eight at head dim 64) run the whole
+    fused call in one workgroup per head with K and V kept in LDS: outputs and
+    log-sum-exp bit for bit those of prepare then attn (longer heads, here
+    2x385x2, take the separate launches)."""
+    import torch
+    w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=3100 + S + D)
+    q, k, v = (to_dev(a) for a in inputs(w))
+    f, lf = sage.sageattn(q, k, v, is_causal=causal, smooth_k=smooth_k, return_lse=True)
+    p = sage.prepare(q, k, v, smooth_k)
+    t, lt = sage.attn(p, w.sm_scale, is_causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f.view(torch.int16), t.view(torch.int16))
+    assert torch.equal(lf.view(torch.int32), lt.view(torch.int32))
+
+
 def test_prepare_reuse_rewrites_the_same_buffers(sage):
     """prepare(reuse=...) writes a previous result's tensors again: same
     storage, same bits as a fresh call, on other inputs of the same shape;
