@@ -185,9 +185,9 @@ size_t sage_fused_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
  * (an extension: the pages' package rejects it). return_lse = 1 also writes lse
  * as sage_attn_lse does (lse non-NULL); return_lse = 0 requires lse NULL (else
  * SAGE_ERR_INVALID_ARGUMENT). o and lse are bit for bit those of sage_prepare
- * followed by sage_attn_ex. Library convention: heads of at most 384 rows (1024
- * at head dim 64) are handled in one launch that keeps the K and V codes on
- * chip; the workspace's contents after a call are unspecified. */
+ * followed by sage_attn_ex. Library convention: heads of at most 384 rows (768
+ * at head dim 64) are handled in one launch that keeps the codes on chip; the
+ * workspace's contents after a call are unspecified. */
 sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sage_tensor* v, const sage_tensor* o,
                             int is_causal, float sm_scale, int return_lse, float* lse, int smooth_k, void* ws,
                             size_t ws_bytes, void* stream);

@@ -699,14 +699,18 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 // A head of at most Short<D>::kTiles key tiles is handled start to end by one
 // workgroup of kShortWaves waves, in one launch: first the prologue's steps for
 // the head, with the arithmetic of its three passes (the same codes and
-// scales), the Q codes and all scales going to the workspace and the K and V
-// codes straight into LDS, in the layout the tile copies above give them; then
-// each wave runs the key loop over those resident tiles for its 32-query
-// blocks. Wave w takes the 32-row blocks w, w + 8, ... in both phases.
+// scales), the K and V scales going to the workspace and every code straight
+// into LDS (K and V in the layout the tile copies above give them, Q in the
+// layout of the query rows); then each wave runs the key loop over the
+// resident tiles for its 32-query blocks. The prologue steps are split into
+// pieces (one tensor of one 32-row block; for V's codes, half of a block's
+// rows at head dim 128) handed to the waves in turn, so they share them
+// evenly; a wave loads its next piece while it works on the current one.
 constexpr int kShortWaves = 8;
 template <int D>
 struct Short {
-  static constexpr int kTiles = D == 128 ? 3 : 8;   // resident K and V tiles that fit in LDS
+  static constexpr int kTiles = D == 128 ? 3 : 6;   // resident K, V and Q that fit in LDS
+  static constexpr int kBlocks = 4 * kTiles;        // 32-row blocks
 };
 
 // Codes of rows 32 (j % 4) + G i + g of K tile j / 4 (channels 8c..8c+7 in
@@ -725,22 +729,37 @@ SAGE_INLINE void put_k_rows(uint8_t* kres, int j, const uint32_t (&lo)[Geo<D>::I
   }
 }
 
+// Codes of query block j into its 32 resident rows: chunk (c / 2) of row r at
+// slot (c / 2) XOR fq(r), as the attention kernel stores its query rows.
+template <int D>
+SAGE_INLINE void put_q_rows(uint8_t* qblk, const uint32_t (&lo)[Geo<D>::I], const uint32_t (&hi)[Geo<D>::I], int c,
+                            int g) {
+  using Gm = Geo<D>;
+#pragma unroll
+  for (int i = 0; i < Gm::I; ++i) {
+    const int r = Gm::G * i + g;
+    *reinterpret_cast<uint2*>(qblk + r * D + ((((c >> 1) ^ Dim<D>::fq(r)) << 4) | ((c & 1) << 3))) =
+        make_uint2(lo[i], hi[i]);
+  }
+}
+
 template <int D, bool kCausal>
 __global__ void __launch_bounds__(64 * kShortWaves, 1)
 short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int smooth_k, float sl2,
-             int8_t* __restrict__ q8, float* __restrict__ q_scale, float* __restrict__ k_scale,
-             float* __restrict__ v_scale, Bf16OutView o, float* __restrict__ lse) {
+             float* __restrict__ k_scale, float* __restrict__ v_scale, Bf16OutView o, float* __restrict__ lse) {
   using Gm = Geo<D>;
   using Dm = Dim<D>;
   constexpr int TB = Dm::kTileBytes, NT = Short<D>::kTiles, NW = kShortWaves;
-  // [K tiles][V tiles][32 query rows per wave]; during the prologue steps the
-  // per-wave channel statistics and the exact-sum digits overlay the V tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NT * TB + NW * 32 * D];
-  __shared__ float s_kmean[D], s_vinv[D], s_vlift[D];
+  constexpr int QB = 32 * D;   // one resident query block
+  // [K tiles][V tiles][query blocks]; during the prologue steps the per-wave
+  // channel statistics and the exact-sum digits overlay the V tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NT * TB + Short<D>::kBlocks * QB];
+  __shared__ float s_kmean[D], s_vinv[D], s_vlift[D], s_qscale[Short<D>::kBlocks];
   static_assert(NW * D * (sizeof(double) + sizeof(float)) <= NT * TB, "statistics overlay");
   static_assert(kExactSlices * kDigits * D * sizeof(long long) <= NT * TB, "digit overlay");
   uint8_t* const kres = lds;
   uint8_t* const vres = lds + NT * TB;
+  uint8_t* const qres = lds + 2 * NT * TB;
   double(*const fsum)[D] = reinterpret_cast<double(*)[D]>(vres);
   float(*const fmx)[D] = reinterpret_cast<float(*)[D]>(vres + NW * D * sizeof(double));
   long long(*const dig)[kDigits][D] = reinterpret_cast<long long(*)[kDigits][D]>(vres);
@@ -754,47 +773,64 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   const uint16_t* kb = k.data + b * k.sb + h * k.sh + 8 * c;
   const uint16_t* vb = v.data + b * v.sb + h * v.sh + 8 * c;
 
-  // ---- Q codes, K codes when smooth_k is off, channel statistics
+  // ---- Q codes, K codes when smooth_k is off, channel statistics: piece
+  // p = 3 j + t is tensor t (Q, K, V) of block j
   double ksum[8];
   float vmax[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ksum[e] = 0.0; vmax[e] = 0.0f; }
-  for (int j = w; j < nb; j += NW) {
+  const int npa = 3 * nb;
+  auto load_piece = [&](int p, Row16 (&r)[Gm::I]) {
+    const int j = p / 3, t = p - 3 * j;
     const int64_t r0 = 32 * (int64_t)j;
+    if (t == 0) {   // Q is read once: nontemporal
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i) {
+        const int64_t row = r0 + Gm::G * i + g;
+        r[i] = row < S ? load16nt(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
+      }
+    } else {
+      const uint16_t* base = t == 1 ? kb : vb;
+      const int64_t ss = t == 1 ? k.ss : v.ss;
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i) {
+        const int64_t row = r0 + Gm::G * i + g;
+        r[i] = row < S ? load16(base + row * ss) : Row16{{0, 0, 0, 0}};
+      }
+    }
+  };
+  Row16 cur[Gm::I];
+  if (w < npa) load_piece(w, cur);
+  for (int p = w; p < npa; p += NW) {
+    Row16 nxt[Gm::I];
+    if (p + NW < npa) load_piece(p + NW, nxt);
+    const int j = p / 3, t = p - 3 * j;
     float x[8 * Gm::I];
 #pragma unroll
-    for (int i = 0; i < Gm::I; ++i) {
-      const int64_t row = r0 + Gm::G * i + g;
-      Row16 r = row < S ? load16nt(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
-      unpack(r, &x[i * 8]);
-    }
-    quant_block_store<D>(x, q8 + (bh * S_pad + r0) * D, q_scale + bh * nb + j, lane);
-#pragma unroll
-    for (int i = 0; i < Gm::I; ++i) {
-      const int64_t row = r0 + Gm::G * i + g;
-      Row16 r = row < S ? load16(kb + row * k.ss) : Row16{{0, 0, 0, 0}};
-      unpack(r, &x[i * 8]);
-    }
-    if (smooth_k) {
-#pragma unroll
-      for (int i = 0; i < Gm::I; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ksum[e] = add_exact_or_nan(ksum[e], (double)x[i * 8 + e]);
-    } else {
+    for (int i = 0; i < Gm::I; ++i) unpack(cur[i], &x[i * 8]);
+    if (t == 0) {
       uint32_t lo[Gm::I], hi[Gm::I];
       const float sc = quant_block_codes<D>(x, lo, hi);
-      if (lane == 0) k_scale[bh * nb + j] = sc;
-      put_k_rows<D>(kres, j, lo, hi, c, g);
+      if (lane == 0) s_qscale[j] = sc;
+      put_q_rows<D>(qres + j * QB, lo, hi, c, g);
+    } else if (t == 1) {
+      if (smooth_k) {
+#pragma unroll
+        for (int i = 0; i < Gm::I; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ksum[e] = add_exact_or_nan(ksum[e], (double)x[i * 8 + e]);
+      } else {
+        uint32_t lo[Gm::I], hi[Gm::I];
+        const float sc = quant_block_codes<D>(x, lo, hi);
+        if (lane == 0) k_scale[bh * nb + j] = sc;
+        put_k_rows<D>(kres, j, lo, hi, c, g);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8 * Gm::I; ++i) vmax[i & 7] = fmaxf(vmax[i & 7], fabsf(x[i]));
     }
 #pragma unroll
-    for (int i = 0; i < Gm::I; ++i) {
-      const int64_t row = r0 + Gm::G * i + g;
-      Row16 r = row < S ? load16(vb + row * v.ss) : Row16{{0, 0, 0, 0}};
-      float y[8];
-      unpack(r, y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vmax[e] = fmaxf(vmax[e], fabsf(y[e]));
-    }
+    for (int i = 0; i < Gm::I; ++i) cur[i] = nxt[i];
   }
   // the wave's statistics, folded over the lanes of a channel, then over the
   // waves in order (every addition checked, as in the three passes)
@@ -850,10 +886,14 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
   __syncthreads();   // the constants are in place; the overlay is free for the V tiles
 
-  // ---- K codes when smooth_k is on, V codes
-  for (int j = w; j < nb; j += NW) {
-    const int64_t r0 = 32 * (int64_t)j;
-    if (smooth_k) {
+  // ---- V codes (piece p < nvp: half p % NH of block p / NH), then K codes
+  // when smooth_k is on (piece nvp + j: block j)
+  constexpr int NH = 8 / Gm::G;   // row halves of a block in the V mapping
+  const int nvp = NH * nb, npb = nvp + (smooth_k ? nb : 0);
+  for (int p = w; p < npb; p += NW) {
+    if (p >= nvp) {
+      const int j = p - nvp;
+      const int64_t r0 = 32 * (int64_t)j;
       float km[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) km[e] = s_kmean[8 * c + e];
@@ -875,11 +915,13 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
       const float sc = quant_block_codes<D>(x, lo, hi);
       if (lane == 0) k_scale[bh * nb + j] = sc;
       put_k_rows<D>(kres, j, lo, hi, c, g);
+      continue;
     }
     // V: lane (c, g) converts rows 32 (j % 4) + 4 G half + 4 g + u (u = 0..3)
     // of tile j / 4, channels 8c..8c+7, as the quantize pass does; a channel's
     // four consecutive keys go to its resident row as one dword, key chunk
     // (r / 16) at slot (r / 16) XOR ((channel / 2) % 8)
+    const int j = p / NH, half = p - NH * j;
     float inv[8], lift[8];
     uint32_t keep[8];
 #pragma unroll
@@ -893,64 +935,53 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
     for (int e = 0; e < 8; ++e) lifted |= lift[e] != 1.0f;
     lifted = __builtin_amdgcn_ballot_w64(lifted) != 0;
     uint8_t* vtile = vres + (j >> 2) * TB;
+    const int rl = 32 * (j & 3) + 4 * Gm::G * half + 4 * g;   // tile row of u = 0
+    uint32_t codes[8];
 #pragma unroll
-    for (int half = 0; half < 8 / Gm::G; ++half) {
-      const int rl = 32 * (j & 3) + 4 * Gm::G * half + 4 * g;   // tile row of u = 0
-      uint32_t codes[8];
+    for (int e = 0; e < 8; ++e) codes[e] = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) codes[e] = 0;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = 32 * (int64_t)j + 4 * Gm::G * half + 4 * g + u;
+      float y[8];
+      if (row < S) unpack(load16(vb + row * v.ss), y);
+      else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t row = r0 + 4 * Gm::G * half + 4 * g + u;
-        float y[8];
-        if (row < S) unpack(load16(vb + row * v.ss), y);
-        else {
+        for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+      }
+      if (lifted) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = 0.0f;
-        }
-        if (lifted) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] *= lift[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[e] * inv[e], y[e + 1] * inv[e + 1], 0, false);
-          codes[e] |= (pk & 0xFFu) << (8 * u);
-          codes[e + 1] |= ((pk >> 8) & 0xFFu) << (8 * u);
-        }
+        for (int e = 0; e < 8; ++e) y[e] *= lift[e];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = 8 * c + e;
-        *reinterpret_cast<uint32_t*>(vtile + ch * kKvTile + ((((rl >> 4) ^ ((ch >> 1) & 7)) << 4) | (rl & 15))) =
-            codes[e] & keep[e];
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[e] * inv[e], y[e + 1] * inv[e + 1], 0, false);
+        codes[e] |= (pk & 0xFFu) << (8 * u);
+        codes[e + 1] |= ((pk >> 8) & 0xFFu) << (8 * u);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = 8 * c + e;
+      *reinterpret_cast<uint32_t*>(vtile + ch * kKvTile + ((((rl >> 4) ^ ((ch >> 1) & 7)) << 4) | (rl & 15))) =
+          codes[e] & keep[e];
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's codes and scales are stored ...
-  __syncthreads();                 // ... and every wave's: the resident tiles are complete
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's scales are stored ...
+  __syncthreads();                 // ... and every wave's: the resident codes are complete
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
   // ---- attention, per 32-query block, over the resident tiles
   const int half = lane >> 5, col = lane & 31;
   const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-  uint8_t* qlds = lds + 2 * NT * TB + w * 32 * D;
-  const uint8_t* qrow = qlds + col * D;
   const int last_valid = (int)(S - (int64_t)(nt - 1) * kKvTile);
   const float* ks = k_scale + bh * nb;
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kBufferWord3);
   const uint32_t no_off[Dm::kCopyInstr] = {};
   for (int j = w; j < nb; j += NW) {
-    // the block's query codes (this wave wrote them above) into the wave's rows
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int r = (1024 / D) * i + lane / Dm::kChunks, cc = lane % Dm::kChunks;
-      const uint4 val = *reinterpret_cast<const uint4*>(q8 + (bh * S_pad + 32 * (int64_t)j + r) * D + cc * 16);
-      *reinterpret_cast<uint4*>(qlds + r * D + ((cc ^ Dm::fq(r)) * 16)) = val;
-    }
-    const int wt = j & 3;                        // the block's place in its 128-query tile
+    const uint8_t* qrow = qres + j * QB + col * D;
+    const int wt = j & 3;                          // the block's place in its 128-query tile
     const int ntw = kCausal ? (j >> 2) + 1 : nt;   // key tiles the block visits
-    float qs = q_scale[bh * nb + j];
+    float qs = s_qscale[j];
     const uint32_t kexact = __builtin_amdgcn_readfirstlane(__float_as_uint(0x1p-7f / (sl2 * qs)));
     asm volatile("" : "+v"(qs));
     uint32_t kmax = 0;
@@ -976,14 +1007,13 @@ bool short_fused_fits(int64_t S, int64_t D) {
 }
 
 hipError_t launch_fused_short(const Bf16View& q, const Bf16View& k, const Bf16View& v, int64_t B, int64_t S,
-                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, int8_t* q8,
-                              float* q_scale, float* k_scale, float* v_scale, const Bf16OutView& o, float* lse,
-                              hipStream_t stream) {
+                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, float* k_scale,
+                              float* v_scale, const Bf16OutView& o, float* lse, hipStream_t stream) {
   const int64_t S_pad = padded_len(S);
   const float sl2 = sm_scale * kLog2e;
 #define SAGE_LAUNCH(D_, CAUSAL_)                                                                               \
   hipLaunchKernelGGL((short_kernel<D_, CAUSAL_>), dim3((unsigned)(B * H)), dim3(64 * kShortWaves), 0, stream, q, k, \
-                     v, H, S, S_pad, smooth_k, sl2, q8, q_scale, k_scale, v_scale, o, lse)
+                     v, H, S, S_pad, smooth_k, sl2, k_scale, v_scale, o, lse)
   if (D == 64) {
     if (causal) SAGE_LAUNCH(64, true);
     else SAGE_LAUNCH(64, false);

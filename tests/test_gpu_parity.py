@@ -733,13 +733,14 @@ def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
 
 @pytest.mark.parametrize("B,S,H,D,causal,smooth_k", [(2, 384, 3, 128, False, True), (1, 300, 2, 128, True, False),
                                                       (3, 129, 2, 128, False, False), (1, 1, 1, 128, False, True),
-                                                      (2, 1000, 2, 64, True, True), (1, 257, 3, 64, False, False),
-                                                      (2, 385, 2, 128, False, True)])
+                                                      (2, 700, 2, 64, True, True), (1, 257, 3, 64, False, False),
+                                                      (2, 768, 1, 64, False, True), (2, 385, 2, 128, False, True),
+                                                      (1, 769, 2, 64, True, False)])
 def test_fused_short_heads_equal_prepare_then_attn(sage, B, S, H, D, causal, smooth_k):
-    """Heads of up to three key tiles (eight at head dim 64) run the whole
-    fused call in one workgroup per head with K and V kept in LDS: outputs and
+    """Heads of up to three key tiles (six at head dim 64) run the whole fused
+    call in one workgroup per head with the codes kept in LDS: outputs and
     log-sum-exp bit for bit those of prepare then attn (longer heads, here
-    2x385x2, take the separate launches)."""
+    2x385x2 and 1x769x2 at head dim 64, take the separate launches)."""
     import torch
     w = synth.custom(B, S, H, D=D, smooth_k=smooth_k, base_seed=3100 + S + D)
     q, k, v = (to_dev(a) for a in inputs(w))
