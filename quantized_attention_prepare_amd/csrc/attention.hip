@@ -448,7 +448,8 @@ SAGE_INLINE void pv_tile(WaveState<D>& st, const uint8_t* vbuf, int half, int co
 // kResident: every K tile of the head is in LDS from lds on (tile t at
 // lds + t TB) and every V tile from vres on, in the layout the copies give
 // them; the loop then copies nothing and passes no barrier, so the waves of a
-// workgroup may run different numbers of tiles.
+// workgroup may run different numbers of tiles. v_scale then points at the
+// head's D scales themselves.
 template <int D, bool kCausal, bool kExact, bool kResident = false>
 SAGE_INLINE void key_loop(uint8_t* lds, uint8_t* vres, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                           const uint32_t (&k_lane_off)[Dim<D>::kCopyInstr],
@@ -554,7 +555,7 @@ SAGE_INLINE void key_loop(uint8_t* lds, uint8_t* vres, __amdgpu_buffer_rsrc_t rk
   if (lse != nullptr && half == 0 && qi < S) lse[bh * S + qi] = (st.m_run + __log2f(l_tot) - kLog2_448) * kLn2;
   if (qi < S) {
     uint16_t* orow = o.data + b * o.sb + qi * o.ss + h * o.sh;
-    const float* vs = v_scale + bh * D;
+    const float* vs = kResident ? v_scale : v_scale + bh * D;   // resident: the head's own scales
 #pragma unroll
     for (int d = 0; d < Dm::kOBlk; ++d) {
 #pragma unroll
@@ -699,9 +700,9 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 // A head of at most Short<D>::kTiles key tiles is handled start to end by one
 // workgroup of kShortWaves waves, in one launch: first the prologue's steps for
 // the head, with the arithmetic of its three passes (the same codes and
-// scales), the K and V scales going to the workspace and every code straight
-// into LDS (K and V in the layout the tile copies above give them, Q in the
-// layout of the query rows); then each wave runs the key loop over the
+// scales), every code and scale kept in LDS (K and V codes in the layout the
+// tile copies above give them, Q codes in the layout of the query rows); then
+// each wave runs the key loop over the
 // resident tiles for its 32-query blocks. The prologue steps are split into
 // pieces (one tensor of one 32-row block; for V's codes, half of a block's
 // rows at head dim 128) handed to the waves in turn, so they share them
@@ -746,7 +747,7 @@ SAGE_INLINE void put_q_rows(uint8_t* qblk, const uint32_t (&lo)[Geo<D>::I], cons
 template <int D, bool kCausal>
 __global__ void __launch_bounds__(64 * kShortWaves, 1)
 short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S_pad, int smooth_k, float sl2,
-             float* __restrict__ k_scale, float* __restrict__ v_scale, Bf16OutView o, float* __restrict__ lse) {
+             Bf16OutView o, float* __restrict__ lse) {
   using Gm = Geo<D>;
   using Dm = Dim<D>;
   constexpr int TB = Dm::kTileBytes, NT = Short<D>::kTiles, NW = kShortWaves;
@@ -754,7 +755,8 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   // [K tiles][V tiles][query blocks]; during the prologue steps the per-wave
   // channel statistics and the exact-sum digits overlay the V tiles
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NT * TB + Short<D>::kBlocks * QB];
-  __shared__ float s_kmean[D], s_vinv[D], s_vlift[D], s_qscale[Short<D>::kBlocks];
+  __shared__ float s_kmean[D], s_vinv[D], s_vlift[D], s_vscale[D];
+  __shared__ __attribute__((aligned(16))) float s_qscale[Short<D>::kBlocks], s_kscale[Short<D>::kBlocks];
   static_assert(NW * D * (sizeof(double) + sizeof(float)) <= NT * TB, "statistics overlay");
   static_assert(kExactSlices * kDigits * D * sizeof(long long) <= NT * TB, "digit overlay");
   uint8_t* const kres = lds;
@@ -822,7 +824,7 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
       } else {
         uint32_t lo[Gm::I], hi[Gm::I];
         const float sc = quant_block_codes<D>(x, lo, hi);
-        if (lane == 0) k_scale[bh * nb + j] = sc;
+        if (lane == 0) s_kscale[j] = sc;
         put_k_rows<D>(kres, j, lo, hi, c, g);
       }
     } else {
@@ -879,7 +881,7 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
   if (tid < D) {
     s_kmean[tid] = smooth_k ? (float)(ssum / (double)S) : 0.0f;
-    v_scale[bh * D + tid] = amax == 0.0f ? 0.0f : amax / 448.0f;
+    s_vscale[tid] = amax == 0.0f ? 0.0f : amax / 448.0f;
     const float lift = amax < kTiny ? kTinyLift : 1.0f;
     s_vinv[tid] = amax == 0.0f ? 0.0f : 448.0f / (amax * lift);
     s_vlift[tid] = lift;
@@ -913,7 +915,7 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
       }
       uint32_t lo[Gm::I], hi[Gm::I];
       const float sc = quant_block_codes<D>(x, lo, hi);
-      if (lane == 0) k_scale[bh * nb + j] = sc;
+      if (lane == 0) s_kscale[j] = sc;
       put_k_rows<D>(kres, j, lo, hi, c, g);
       continue;
     }
@@ -966,15 +968,13 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
           codes[e] & keep[e];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's scales are stored ...
-  __syncthreads();                 // ... and every wave's: the resident codes are complete
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __syncthreads();   // every wave's codes and scales are in place
 
   // ---- attention, per 32-query block, over the resident tiles
   const int half = lane >> 5, col = lane & 31;
   const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
   const int last_valid = (int)(S - (int64_t)(nt - 1) * kKvTile);
-  const float* ks = k_scale + bh * nb;
+  const float* ks = s_kscale;
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kBufferWord3);
   const uint32_t no_off[Dm::kCopyInstr] = {};
   for (int j = w; j < nb; j += NW) {
@@ -990,12 +990,12 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
     for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
     if (__builtin_expect(__builtin_amdgcn_readfirstlane(kmax) >= kexact, 0))
       key_loop<D, kCausal, true, true>(kres, vres, none, none, no_off, no_off, ks, qs, sl2, qrow, prow, wt, half, col,
-                                       ntw, nt, last_valid, (uint32_t)S_pad, 32 * (int64_t)j, S, bh, b, h, v_scale, o,
-                                       lse);
+                                       ntw, nt, last_valid, (uint32_t)S_pad, 32 * (int64_t)j, S, bh, b, h, s_vscale,
+                                       o, lse);
     else
       key_loop<D, kCausal, false, true>(kres, vres, none, none, no_off, no_off, ks, qs, sl2, qrow, prow, wt, half,
                                         col, ntw, nt, last_valid, (uint32_t)S_pad, 32 * (int64_t)j, S, bh, b, h,
-                                        v_scale, o, lse);
+                                        s_vscale, o, lse);
   }
 }
 
@@ -1007,13 +1007,13 @@ bool short_fused_fits(int64_t S, int64_t D) {
 }
 
 hipError_t launch_fused_short(const Bf16View& q, const Bf16View& k, const Bf16View& v, int64_t B, int64_t S,
-                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, float* k_scale,
-                              float* v_scale, const Bf16OutView& o, float* lse, hipStream_t stream) {
+                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, const Bf16OutView& o,
+                              float* lse, hipStream_t stream) {
   const int64_t S_pad = padded_len(S);
   const float sl2 = sm_scale * kLog2e;
 #define SAGE_LAUNCH(D_, CAUSAL_)                                                                               \
   hipLaunchKernelGGL((short_kernel<D_, CAUSAL_>), dim3((unsigned)(B * H)), dim3(64 * kShortWaves), 0, stream, q, k, \
-                     v, H, S, S_pad, smooth_k, sl2, k_scale, v_scale, o, lse)
+                     v, H, S, S_pad, smooth_k, sl2, o, lse)
   if (D == 64) {
     if (causal) SAGE_LAUNCH(64, true);
     else SAGE_LAUNCH(64, false);

@@ -367,8 +367,7 @@ sage_status sage_attn_fused(const sage_tensor* q, const sage_tensor* k, const sa
   sage::Bf16OutView ov{static_cast<uint16_t*>(o->data), o->stride[0], o->stride[1], o->stride[2]};
   if (sage::short_fused_fits(S, q->size[3])) {
     hipError_t e = sage::launch_fused_short(view(q), view(k), view(v), B, S, H, q->size[3], smooth_k ? 1 : 0,
-                                            sm_scale, is_causal != 0, w.k_scale, w.v_scale, ov,
-                                            return_lse ? lse : nullptr, st);
+                                            sm_scale, is_causal != 0, ov, return_lse ? lse : nullptr, st);
     if (e != hipSuccess) return fail(SAGE_ERR_DEVICE, "fused launch failed: %s", hipGetErrorString(e));
     return ok();
   }

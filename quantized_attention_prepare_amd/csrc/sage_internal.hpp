@@ -64,12 +64,12 @@ hipError_t launch_attention(const int8_t* q8, const float* q_scale, const int8_t
                             float sm_scale, bool causal, const Bf16OutView& o, float* lse, hipStream_t stream);
 
 // The whole forward in one launch for short heads (one workgroup per head; the
-// Q, K and V codes never leave LDS): whether a head of S rows fits, and the
-// launch. k_scale and v_scale receive what the prologue writes for them.
+// codes and scales never leave LDS): whether a head of S rows fits, and the
+// launch.
 bool short_fused_fits(int64_t S, int64_t D);
 hipError_t launch_fused_short(const Bf16View& q, const Bf16View& k, const Bf16View& v, int64_t B, int64_t S,
-                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, float* k_scale,
-                              float* v_scale, const Bf16OutView& o, float* lse, hipStream_t stream);
+                              int64_t H, int64_t D, int smooth_k, float sm_scale, bool causal, const Bf16OutView& o,
+                              float* lse, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
