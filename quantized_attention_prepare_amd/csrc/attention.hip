@@ -703,15 +703,18 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 // scales), every code and scale kept in LDS (K and V codes in the layout the
 // tile copies above give them, Q codes in the layout of the query rows); then
 // each wave runs the key loop over the
-// resident tiles for its 32-query blocks. The prologue steps are split into
-// pieces (one tensor of one 32-row block; for V's codes, half of a block's
-// rows at head dim 128) handed to the waves in turn, so they share them
-// evenly; a wave loads its next piece while it works on the current one.
+// resident tiles for its 32-query blocks. The statistics pass is split into
+// pieces (one tensor of one 32-row block) handed to the waves in turn, so
+// they share them evenly; a wave loads its next piece while it works on the
+// current one, and keeps the V blocks it read in registers until their codes
+// can be formed.
 constexpr int kShortWaves = 8;
 template <int D>
 struct Short {
   static constexpr int kTiles = D == 128 ? 3 : 6;   // resident K, V and Q that fit in LDS
   static constexpr int kBlocks = 4 * kTiles;        // 32-row blocks
+  static constexpr int kVPerWave = (kBlocks + kShortWaves - 1) / kShortWaves;   // V blocks a wave reads
+  static constexpr int kVKept = D == 128 ? 1 : kVPerWave;   // of them held in registers (the rest read again)
 };
 
 // Codes of rows 32 (j % 4) + G i + g of K tile j / 4 (channels 8c..8c+7 in
@@ -791,21 +794,35 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
         const int64_t row = r0 + Gm::G * i + g;
         r[i] = row < S ? load16nt(qb + row * q.ss) : Row16{{0, 0, 0, 0}};
       }
-    } else {
-      const uint16_t* base = t == 1 ? kb : vb;
-      const int64_t ss = t == 1 ? k.ss : v.ss;
+    } else if (t == 1) {
 #pragma unroll
       for (int i = 0; i < Gm::I; ++i) {
         const int64_t row = r0 + Gm::G * i + g;
-        r[i] = row < S ? load16(base + row * ss) : Row16{{0, 0, 0, 0}};
+        r[i] = row < S ? load16(kb + row * k.ss) : Row16{{0, 0, 0, 0}};
+      }
+    } else {   // V in the row order of its encoding below: slot i is row 4 G (i / 4) + 4 g + i % 4
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i) {
+        const int64_t row = r0 + 4 * Gm::G * (i >> 2) + 4 * g + (i & 3);
+        r[i] = row < S ? load16(vb + row * v.ss) : Row16{{0, 0, 0, 0}};
       }
     }
   };
+  // The V blocks a wave reads (pieces 3 j + 2 = w mod NW: j = j0, j0 + NW,
+  // ...) stay in its registers until their codes can be formed (the first NK
+  // of them; the others are read again then).
+  constexpr int NV = Short<D>::kVPerWave, NK = Short<D>::kVKept;
+  const int j0 = (3 * (w + NW - 2)) % NW;   // 3 is its own inverse mod 8
+  static_assert(NW == 8, "the V block of a wave assumes eight waves");
+  Row16 vkeep[NK][Gm::I];
+  // the next piece is loaded during the current one where registers allow
+  constexpr bool kAhead = D == 64;
   Row16 cur[Gm::I];
-  if (w < npa) load_piece(w, cur);
+  if (kAhead && w < npa) load_piece(w, cur);
   for (int p = w; p < npa; p += NW) {
     Row16 nxt[Gm::I];
-    if (p + NW < npa) load_piece(p + NW, nxt);
+    if (kAhead && p + NW < npa) load_piece(p + NW, nxt);
+    if (!kAhead) load_piece(p, cur);
     const int j = p / 3, t = p - 3 * j;
     float x[8 * Gm::I];
 #pragma unroll
@@ -830,9 +847,18 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
     } else {
 #pragma unroll
       for (int i = 0; i < 8 * Gm::I; ++i) vmax[i & 7] = fmaxf(vmax[i & 7], fabsf(x[i]));
-    }
+      const int slot = (j - j0) / NW;   // uniform over the wave
 #pragma unroll
-    for (int i = 0; i < Gm::I; ++i) cur[i] = nxt[i];
+      for (int sl = 0; sl < NK; ++sl)
+        if (slot == sl) {
+#pragma unroll
+          for (int i = 0; i < Gm::I; ++i) vkeep[sl][i] = cur[i];
+        }
+    }
+    if (kAhead) {
+#pragma unroll
+      for (int i = 0; i < Gm::I; ++i) cur[i] = nxt[i];
+    }
   }
   // the wave's statistics, folded over the lanes of a channel, then over the
   // waves in order (every addition checked, as in the three passes)
@@ -888,17 +914,14 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
   }
   __syncthreads();   // the constants are in place; the overlay is free for the V tiles
 
-  // ---- V codes (piece p < nvp: half p % NH of block p / NH), then K codes
-  // when smooth_k is on (piece nvp + j: block j)
-  constexpr int NH = 8 / Gm::G;   // row halves of a block in the V mapping
-  const int nvp = NH * nb, npb = nvp + (smooth_k ? nb : 0);
-  for (int p = w; p < npb; p += NW) {
-    if (p >= nvp) {
-      const int j = p - nvp;
-      const int64_t r0 = 32 * (int64_t)j;
-      float km[8];
+  // ---- K codes when smooth_k is on (block j by wave j mod NW), then the
+  // codes of the wave's V blocks from its registers
+  if (smooth_k) {
+    float km[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) km[e] = s_kmean[8 * c + e];
+    for (int e = 0; e < 8; ++e) km[e] = s_kmean[8 * c + e];
+    for (int j = w; j < nb; j += NW) {
+      const int64_t r0 = 32 * (int64_t)j;
       float x[8 * Gm::I];
 #pragma unroll
       for (int i = 0; i < Gm::I; ++i) {
@@ -917,13 +940,13 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
       const float sc = quant_block_codes<D>(x, lo, hi);
       if (lane == 0) s_kscale[j] = sc;
       put_k_rows<D>(kres, j, lo, hi, c, g);
-      continue;
     }
+  }
+  {
     // V: lane (c, g) converts rows 32 (j % 4) + 4 G half + 4 g + u (u = 0..3)
     // of tile j / 4, channels 8c..8c+7, as the quantize pass does; a channel's
     // four consecutive keys go to its resident row as one dword, key chunk
     // (r / 16) at slot (r / 16) XOR ((channel / 2) % 8)
-    const int j = p / NH, half = p - NH * j;
     float inv[8], lift[8];
     uint32_t keep[8];
 #pragma unroll
@@ -936,36 +959,48 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 #pragma unroll
     for (int e = 0; e < 8; ++e) lifted |= lift[e] != 1.0f;
     lifted = __builtin_amdgcn_ballot_w64(lifted) != 0;
-    uint8_t* vtile = vres + (j >> 2) * TB;
-    const int rl = 32 * (j & 3) + 4 * Gm::G * half + 4 * g;   // tile row of u = 0
-    uint32_t codes[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) codes[e] = 0;
+    for (int sl = 0; sl < NV; ++sl) {
+      const int j = j0 + NW * sl;
+      if (j >= nb) break;
+      uint8_t* vtile = vres + (j >> 2) * TB;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t row = 32 * (int64_t)j + 4 * Gm::G * half + 4 * g + u;
-      float y[8];
-      if (row < S) unpack(load16(vb + row * v.ss), y);
-      else {
+      for (int half = 0; half < 8 / Gm::G; ++half) {
+        const int rl = 32 * (j & 3) + 4 * Gm::G * half + 4 * g;   // tile row of u = 0
+        uint32_t codes[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) codes[e] = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float y[8];
+          if (sl < NK) {
+            unpack(vkeep[sl < NK ? sl : 0][4 * half + u], y);   // padding rows were read as zeros
+          } else {
+            const int64_t row = 32 * (int64_t)j + 4 * Gm::G * half + 4 * g + u;
+            if (row < S) unpack(load16(vb + row * v.ss), y);
+            else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+            }
+          }
+          if (lifted) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= lift[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[e] * inv[e], y[e + 1] * inv[e + 1], 0, false);
+            codes[e] |= (pk & 0xFFu) << (8 * u);
+            codes[e + 1] |= ((pk >> 8) & 0xFFu) << (8 * u);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = 8 * c + e;
+          *reinterpret_cast<uint32_t*>(vtile + ch * kKvTile + ((((rl >> 4) ^ ((ch >> 1) & 7)) << 4) | (rl & 15))) =
+              codes[e] & keep[e];
+        }
       }
-      if (lifted) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= lift[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[e] * inv[e], y[e + 1] * inv[e + 1], 0, false);
-        codes[e] |= (pk & 0xFFu) << (8 * u);
-        codes[e + 1] |= ((pk >> 8) & 0xFFu) << (8 * u);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ch = 8 * c + e;
-      *reinterpret_cast<uint32_t*>(vtile + ch * kKvTile + ((((rl >> 4) ^ ((ch >> 1) & 7)) << 4) | (rl & 15))) =
-          codes[e] & keep[e];
     }
   }
   __syncthreads();   // every wave's codes and scales are in place
