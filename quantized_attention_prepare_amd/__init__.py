@@ -122,9 +122,15 @@ def padded_len(S: int) -> int:
     return int(lib().sage_padded_len(S))
 
 
+_DTYPE_CODES = {}
+_I64x4 = ctypes.c_int64 * 4
+
+
 def _dtype_code(t) -> int:
-    import torch
-    return {torch.bfloat16: 1, torch.float16: 2, torch.float32: 3}.get(t.dtype, 0)
+    if not _DTYPE_CODES:
+        import torch
+        _DTYPE_CODES.update({torch.bfloat16: 1, torch.float16: 2, torch.float32: 3})
+    return _DTYPE_CODES.get(t.dtype, 0)
 
 
 def describe(t, layout: str = "NHD") -> SageTensor:
@@ -132,14 +138,14 @@ def describe(t, layout: str = "NHD") -> SageTensor:
     if t.dim() != 4:
         raise ValueError("expected a 4-D tensor")
     if layout == "NHD":
-        size, stride = list(t.shape), list(t.stride())
+        size, stride = t.shape, t.stride()
     elif layout == "HND":
         B, H, S, D = t.shape
         sb, sh, ss, sd = t.stride()
-        size, stride = [B, S, H, D], [sb, ss, sh, sd]
+        size, stride = (B, S, H, D), (sb, ss, sh, sd)
     else:
         raise ValueError(f"tensor_layout must be 'NHD' or 'HND', not {layout!r}")
-    return SageTensor(t.data_ptr(), _dtype_code(t), (ctypes.c_int64 * 4)(*size), (ctypes.c_int64 * 4)(*stride))
+    return SageTensor(t.data_ptr(), _dtype_code(t), _I64x4(*size), _I64x4(*stride))
 
 
 def _stream(stream):
@@ -157,12 +163,13 @@ def _gpu_of(*tensors, stream=None) -> int:
     for t in tensors:
         if t is None:
             continue
-        if not t.is_cuda:
+        dev = t.get_device()   # -1 for a host tensor
+        if dev < 0 or not t.is_cuda:
             raise ValueError("every tensor must be on a GPU: the library takes device pointers")
         if idx is None:
-            idx = t.device.index
-        elif t.device.index != idx:
-            raise ValueError(f"tensors on different GPUs ({idx} and {t.device.index})")
+            idx = dev
+        elif dev != idx:
+            raise ValueError(f"tensors on different GPUs ({idx} and {dev})")
     if stream is not None and idx is not None and stream.device.index != idx:
         raise ValueError(f"the stream belongs to GPU {stream.device.index}, the tensors to GPU {idx}")
     return idx
@@ -170,6 +177,14 @@ def _gpu_of(*tensors, stream=None) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _on_device(idx):
+    """torch.cuda.device(idx), entered only when idx is not already current."""
+    import torch
+    if idx is None or idx == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(idx)
 
 
 def _alloc_on(stream):
@@ -190,7 +205,7 @@ def prepare(q, k, v, smooth_k: bool = True, layout: str = "NHD", stream=None, re
     import torch
     reused = [reuse[key] for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale", "k_mean", "_ws")] \
         if reuse is not None else []
-    with torch.cuda.device(_gpu_of(q, k, v, *reused, stream=stream)):
+    with _on_device(_gpu_of(q, k, v, *reused, stream=stream)):
         return _prepare(q, k, v, smooth_k, layout, stream, reuse)
 
 
@@ -237,7 +252,7 @@ def attn(prep: dict, sm_scale: float, out=None, stream=None, return_lse: bool = 
     is_causal: query i sees keys 0 .. i (sage_attn_ex)."""
     import torch
     tensors = [prep[key] for key in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale")]
-    with torch.cuda.device(_gpu_of(*tensors, out, lse, stream=stream)):
+    with _on_device(_gpu_of(*tensors, out, lse, stream=stream)):
         return _attn(prep, sm_scale, out, stream, return_lse, lse, is_causal)
 
 
@@ -276,8 +291,7 @@ def sageattn(q, k, v, tensor_layout: str = "NHD", is_causal: bool = False, sm_sc
     returns the rows' log-sum-exp of the dequantized scores, float32 [B, H, S]
     (both extensions: the pages' sageattn rejects them).
     """
-    import torch
-    with torch.cuda.device(_gpu_of(q, k, v, out, workspace, stream=stream)):
+    with _on_device(_gpu_of(q, k, v, out, workspace, stream=stream)):
         return _sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse, smooth_k, out, workspace, stream)
 
 
@@ -288,13 +302,16 @@ def _sageattn(q, k, v, tensor_layout, is_causal, sm_scale, return_lse, smooth_k,
     tq, tk, tv = describe(q, tensor_layout), describe(k, tensor_layout), describe(v, tensor_layout)
     B, S, H, D = tq.size
     L = lib()
-    nws = int(L.sage_fused_workspace_bytes(B, S, H, D))
-    with _alloc_on(stream):
-        if out is None:
-            out = torch.empty_like(q)
-        if workspace is None:
-            workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = None
+    if out is None or workspace is None or return_lse:   # the library itself allocates nothing
+        with _alloc_on(stream):
+            if out is None:
+                out = torch.empty_like(q)
+            if workspace is None:
+                nws = int(L.sage_fused_workspace_bytes(B, S, H, D))
+                workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+            if return_lse:
+                lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     to = describe(out, tensor_layout)
     check(L.sage_attn_fused(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), int(bool(is_causal)),
                             float(sm_scale), int(bool(return_lse)), _ptr(lse), int(bool(smooth_k)), _ptr(workspace),

@@ -677,17 +677,18 @@ def test_tensors_past_2_31_elements_hnd(sage):
     torch.cuda.empty_cache()
 
 
-def test_fused_calls_replay_from_a_hip_graph(sage):
+@pytest.mark.parametrize("S", [700, 300])
+def test_fused_calls_replay_from_a_hip_graph(sage, S):
     """sageattn, causal and not, captured in one HIP graph (the library launches
     kernels only: no allocation, memset or synchronisation inside) and replayed
     three times with eager work in between: every replay equals the eager result
-    bit for bit."""
+    bit for bit. 700 tokens take the separate launches, 300 the one-launch form."""
     import torch
-    w = synth.custom(2, 700, 3, smooth_k=True, base_seed=6200)
+    w = synth.custom(2, S, 3, smooth_k=True, base_seed=6200 + S)
     q, k, v = (to_dev(a) for a in inputs(w))
     ref = [sage.sageattn(q, k, v, is_causal=c, sm_scale=w.sm_scale, return_lse=True) for c in (False, True)]
     torch.cuda.synchronize()
-    nws = sage.fused_workspace_bytes(2, 700, 3, 128)
+    nws = sage.fused_workspace_bytes(2, S, 3, 128)
     ws = [torch.empty(nws, dtype=torch.uint8, device="cuda") for _ in range(2)]
     outs = [torch.empty_like(q) for _ in range(2)]
     side = torch.cuda.Stream()
