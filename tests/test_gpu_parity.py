@@ -736,7 +736,7 @@ def test_fused_equals_prepare_then_attn_and_is_deterministic(sage):
                                                       (3, 129, 2, 128, False, False), (1, 1, 1, 128, False, True),
                                                       (2, 700, 2, 64, True, True), (1, 257, 3, 64, False, False),
                                                       (2, 768, 1, 64, False, True), (2, 385, 2, 128, False, True),
-                                                      (1, 769, 2, 64, True, False)])
+                                                      (1, 769, 2, 64, True, False), (6, 128, 50, 128, True, True)])
 def test_fused_short_heads_equal_prepare_then_attn(sage, B, S, H, D, causal, smooth_k):
     """Heads of up to three key tiles (six at head dim 64) run the whole fused
     call in one workgroup per head with the codes kept in LDS: outputs and
