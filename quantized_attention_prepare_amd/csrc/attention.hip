@@ -702,12 +702,13 @@ attn_kernel(const int8_t* __restrict__ q8, const float* __restrict__ q_scale, co
 // the head, with the arithmetic of its three passes (the same codes and
 // scales), every code and scale kept in LDS (K and V codes in the layout the
 // tile copies above give them, Q codes in the layout of the query rows); then
-// each wave runs the key loop over the
-// resident tiles for its 32-query blocks. The statistics pass is split into
-// pieces (one tensor of one 32-row block) handed to the waves in turn, so
-// they share them evenly; a wave loads its next piece while it works on the
-// current one, and keeps the V blocks it read in registers until their codes
-// can be formed.
+// each wave runs the key loop over the resident tiles for its 32-query blocks.
+// The statistics pass is split into pieces (one tensor of one 32-row block)
+// handed to the waves in turn, so they share them evenly. At head dim 64 a
+// wave loads its next piece while it works on the current one and keeps every
+// V block it read in registers until the V codes can be formed; at head dim
+// 128, where registers are scarcer, it keeps its first V block and reads any
+// other one again.
 constexpr int kShortWaves = 8;
 template <int D>
 struct Short {
