@@ -753,6 +753,21 @@ def test_fused_short_heads_equal_prepare_then_attn(sage, B, S, H, D, causal, smo
     assert torch.equal(lf.view(torch.int32), lt.view(torch.int32))
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_fused_short_heads_hnd_equal_prepare_then_attn(sage, D, causal):
+    """The one-launch form on HND inputs ([B, H, S, D]) into an HND output: the
+    same bits as prepare then attn on the same layout."""
+    import torch
+    w = synth.custom(2, 333, 3, D=D, smooth_k=True, base_seed=3400 + D)
+    q, k, v = (to_dev(a).permute(0, 2, 1, 3).contiguous() for a in inputs(w))
+    f, lf = sage.sageattn(q, k, v, tensor_layout="HND", is_causal=causal, return_lse=True)
+    p = sage.prepare(q, k, v, True, layout="HND")
+    t, lt = sage.attn(p, w.sm_scale, is_causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f.permute(0, 2, 1, 3).contiguous().view(torch.int16), t.view(torch.int16))
+    assert torch.equal(lf.view(torch.int32), lt.view(torch.int32))
+
+
 def test_prepare_reuse_rewrites_the_same_buffers(sage):
     """prepare(reuse=...) writes a previous result's tensors again: same
     storage, same bits as a fresh call, on other inputs of the same shape;
