@@ -974,7 +974,7 @@ short_kernel(Bf16View q, Bf16View k, Bf16View v, int64_t H, int64_t S, int64_t S
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           float y[8];
-          if (sl < NK) {
+          if (sl < NK) {   // (the index is clamped only so that the branch not taken stays in bounds)
             unpack(vkeep[sl < NK ? sl : 0][4 * half + u], y);   // padding rows were read as zeros
           } else {
             const int64_t row = 32 * (int64_t)j + 4 * Gm::G * half + 4 * g + u;
